@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of the fused MoE layer on one MI355X.
+
+One step = one pass of the whole layer over one batch of synthetic tokens,
+inputs resident in HBM: moe_route (router softmax + top-k on fp32 logits) and
+moe_forward (alignment, [fp8 activation quant], GEMM1 + SiLU-mul epilogue,
+GEMM2 with the router weight, top-k combine).  The fp8 workload is handed its
+routing, as the pages' block-fp8 test is, so its step is moe_forward alone.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+Prints one JSON line.  ``value`` is tokens/s of the whole step; ``roofline``
+describes the dominant kernel (GEMM1), timed with HIP events recorded on the
+stream it runs on; ``cpu_baseline`` is the fp64 oracle on a bounded token
+sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s % of peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "fp8", "skew"])
+    ap.add_argument("--tokens", type=int, default=None, help="use the first T tokens of the workload")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--path", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region run one plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_layer_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, digest: str):
+    """HBM bytes per GEMM1 launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 4 and not line.startswith("#") and f[0] == workload and f[1] == digest:
+            return float(f[3])
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this layer is measured on a "
+              "single MI355X; multi-GPU sharding is described, not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_layer_amd import ops
+    from moe_layer_amd.workloads import CONFIGS, Workload
+
+    d = torch.device("cuda", 0)
+    cfg = CONFIGS[args.workload]
+    if args.tokens:
+        cfg = cfg.with_tokens(args.tokens)
+    wl = Workload(cfg)
+    fp8 = cfg.wdtype == "fp8"
+    T, E, H, I, k = cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk
+    log(f"workload {cfg.name} T={T} E={E} H={H} I={I} k={k} {cfg.wdtype}")
+
+    x = torch.from_numpy(wl.x_bf16_bits().view(np.int16)).view(torch.bfloat16).to(d)
+    if cfg.routing == "logits":
+        logits = torch.from_numpy(wl.logits()).to(d)
+        ids, tw = ops.moe_route(logits, k)
+    else:
+        logits = None
+        ids_np, tw_np = wl.given_routing()
+        ids = torch.from_numpy(ids_np).to(d)
+        tw = torch.from_numpy(tw_np).to(d)
+    torch.cuda.synchronize()
+    ids_host = ids.cpu().numpy()
+    active = np.unique(ids_host[(ids_host >= 0) & (ids_host < E)])
+    log(f"{len(active)} active experts; drawing and uploading their weights")
+
+    if fp8:
+        w13 = torch.zeros((E, 2 * I, H), dtype=torch.uint8, device=d)
+        w2 = torch.zeros((E, H, I), dtype=torch.uint8, device=d)
+        s13 = torch.ones((E, 2 * I // 128, H // 128), dtype=torch.float32, device=d)
+        s2 = torch.ones((E, H // 128, I // 128), dtype=torch.float32, device=d)
+    else:
+        w13 = torch.zeros((E, 2 * I, H), dtype=torch.bfloat16, device=d)
+        w2 = torch.zeros((E, H, I), dtype=torch.bfloat16, device=d)
+        s13 = s2 = None
+
+    # the CPU-baseline sample: the first n tokens (at most 16, and few enough
+    # that they route to at most 96 experts) and the experts they route to
+    n_cpu = args.cpu_sample_tokens or 1
+    if not args.cpu_sample_tokens:
+        while n_cpu < min(T, 16) and len(np.unique(ids_host[:n_cpu + 1])) <= 96:
+            n_cpu += 1
+    cpu_experts = set(np.unique(ids_host[:n_cpu]).tolist())
+    host_keep = {}
+    t0 = time.time()
+
+    def put(e, w):
+        c13, sc13, c2, sc2 = w
+        if fp8:
+            w13[e].copy_(torch.from_numpy(c13))
+            w2[e].copy_(torch.from_numpy(c2))
+            s13[e].copy_(torch.from_numpy(sc13))
+            s2[e].copy_(torch.from_numpy(sc2))
+        else:
+            w13[e].copy_(torch.from_numpy(c13.view(np.int16)).view(torch.bfloat16))
+            w2[e].copy_(torch.from_numpy(c2.view(np.int16)).view(torch.bfloat16))
+        if e in cpu_experts and not args.no_cpu_baseline:
+            host_keep[e] = w
+
+    wl.expert_weights_many(active.tolist(), put)
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f}s")
+
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+    fargs = ops.forward_args(x, w13, w2, ids, tw, s13, s2, out, args.path, args.block_m)
+    plan = ops.moe_plan(fargs)
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=d)
+    lib = ops.lib()
+    import ctypes as C
+
+    def step():
+        if logits is not None:
+            ops.moe_route(logits, k, True, ids, tw)
+        st = lib.moe_forward(C.byref(fargs), C.c_void_p(ws.data_ptr()), ws.numel(),
+                             C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(ops.status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-stage durations on the stream the kernels run on
+    n_ev = ops.MOE_NUM_STAGES + 1
+    stage_ms = np.zeros(ops.MOE_NUM_STAGES)
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        ops.moe_forward_profiled(fargs, ws, evs)
+        torch.cuda.synchronize()
+        stage_ms += np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(ops.MOE_NUM_STAGES)])
+    stage_ms /= args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=d)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- algorithmic work ---------------------------------------------------
+    bw = 1 if fp8 else 2
+    na = len(active)
+    R = T * k
+    w13_bytes = na * 2 * I * H * bw + (na * (2 * I // 128) * (H // 128) * 4 if fp8 else 0)
+    w2_bytes = na * H * I * bw + (na * (H // 128) * (I // 128) * 4 if fp8 else 0)
+    x_bytes = T * H * 2
+    out_bytes = T * H * 2
+    route_bytes = T * k * 8 + (T * E * 4 if logits is not None else 0)
+    layer_bytes = w13_bytes + w2_bytes + x_bytes + out_bytes + route_bytes
+    layer_flops = 6.0 * R * H * I
+    # GEMM1: weights of the active experts, activations in, intermediate out
+    g1_bytes = w13_bytes + (T * H * (1 + 4 / 128) if fp8 else x_bytes) + R * I * (1 + 4 / 128 if fp8 else 2)
+    g1_flops = 4.0 * R * H * I
+    g1_ms = stage_ms[2]
+    decode_like = layer_flops / layer_bytes < (MFMA_PEAK_TFLOPS[cfg.wdtype] / HBM_PEAK_GBS) * 1e3
+    if decode_like:
+        achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = g1_flops / (g1_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[cfg.wdtype]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    digest = kernel_source_digest()
+    roof["traffic"] = read_traffic(cfg.name if not args.tokens else f"{cfg.name}@{T}", digest)
+    roof["kernel"] = "gemm1_small_kernel (GEMM1 + SiLU-mul epilogue)"
+    roof["kernel_ms"] = round(float(g1_ms), 5)
+    roof["algorithmic_per_launch"] = g1_bytes if decode_like else g1_flops
+
+    # ---- CPU baseline: the oracle on a bounded sample ---------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, wl, ids_host, tw.cpu().numpy(), host_keep, n_cpu, logits is not None)
+
+    rec = {
+        "metric": METRIC, "value": round(T / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.wdtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name} MoE layer T={T} E={E} H={H} I={I} topk={k} {cfg.wdtype}",
+                   "T": T, "E": E, "H": H, "I": I, "topk": k, "weights": cfg.wdtype,
+                   "block_m": plan["block_m"], "path": ["auto", "small_m", "large_m"][plan["path"]],
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layer": {"active_experts": int(na), "algorithmic_bytes": int(layer_bytes), "flops": layer_flops,
+                  "hbm_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg.wdtype], 4),
+                  "stage_ms": {n: round(float(v), 5) for n, v in zip(ops.STAGE_NAMES, stage_ms)},
+                  "kernel_digest": digest},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(cfg, wl, ids, tw32, host_w, n, routed_from_logits):
+    """Time the fp64 oracle (route + forward) on the first n tokens."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    E, H, I = cfg.E, cfg.H, cfg.I
+    fp8 = cfg.wdtype == "fp8"
+    x64 = wl.x_exact()[:n]
+    # only the sample's experts, renumbered 0..m-1 (ids are remapped the same way)
+    experts = sorted(host_w)
+    remap = np.full(E, -1, dtype=np.int64)
+    remap[experts] = np.arange(len(experts))
+    w13 = np.empty((len(experts), 2 * I, H))
+    w2 = np.empty((len(experts), H, I))
+    for i, e in enumerate(experts):
+        c13, s13, c2, s2 = host_w[e]
+        if fp8:
+            w13[i], w2[i] = O.dequant_block(c13, s13), O.dequant_block(c2, s2)
+        else:
+            w13[i], w2[i] = O.bf16_bits_to_f64(c13), O.bf16_bits_to_f64(c2)
+    lg = wl.logits()[:n] if routed_from_logits else None
+    reps, t_total = 0, 0.0
+    while reps < 3 or (t_total < 10.0 and reps < 50):
+        t0 = time.perf_counter()
+        if lg is not None:
+            ids_o, tw_o = O.route(lg, cfg.topk)
+        else:
+            ids_o, tw_o = ids[:n], tw32[:n].astype(np.float64)
+        O.forward(x64, w13, w2, remap[ids_o], tw_o, fp8=fp8)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    t = t_total / reps
+    return {"value": round(n / t, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens, route + forward in fp64, mean of {reps} runs "
+                      f"({t:.2f} s each)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+/*
+ * moe.h — C ABI of libmoe_mi355x.so, a fused Mixture-of-Experts layer for
+ * AMD MI355X (CDNA4, gfx950).
+ *
+ * The layer follows the fused-MoE pipeline described in
+ *   [P1] kinachrichten.com, "AWS erklärt zwei Kernel-Optimierungen, die den
+ *        Durchsatz von SageMaker AI auf H200 steigern" (sections "Warum
+ *        MoE-Kernel so wichtig sind", "Swap-AB", "Backend-Wechsel für
+ *        FP8-Modelle"), and
+ *   [P2] blog.secrett2633.cloud, analysis of vLLM PR #64760 "sorted-A TMA
+ *        for FP8 MoE" (section 1.1: the sorted-A path and its block-fp8
+ *        test; section 1.2: the fused SiLU-mul-FP8-quant kernel).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense and row-major.  Device pointers must be 16-byte
+ *     aligned.  bf16 tensors are passed as raw 16-bit words, fp8 tensors as
+ *     raw OCP E4M3FN bytes (max 448, no infinities).
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     retains a pointer, keeps no state between calls and may be called from
+ *     several host threads at once.
+ *   - All device work is enqueued on the caller's stream, in order; nothing
+ *     synchronises the host.  Results are valid once the stream reaches them.
+ *     Calls that share a workspace or output buffer must be ordered by the
+ *     caller (same stream, or events).
+ *   - Every entry point validates its arguments on the host before enqueuing
+ *     any work and returns a status; on an error nothing is enqueued, except
+ *     MOE_ERR_HIP, which reports a failed launch.  T == 0 is a valid no-op.
+ *   - Expert ids outside [0, E) are "not routed": they take no row, contribute
+ *     nothing to the output, and their inverse-permutation entry is -1 (the
+ *     expert_map convention of P2 section 1.1).  Duplicate ids within a token
+ *     are allowed and each slot counts.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_API __attribute__((visibility("default")))
+
+/* status codes */
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG (-1)  /* null/misaligned pointer, negative size, topk out of range ... */
+#define MOE_ERR_UNSUPPORTED (-2)  /* valid request outside what the kernels implement (see limits) */
+#define MOE_ERR_WORKSPACE   (-3)  /* workspace smaller than moe_forward_workspace() */
+#define MOE_ERR_HIP         (-4)  /* a kernel launch failed */
+
+/* weight element types */
+#define MOE_WDTYPE_BF16      0   /* w13/w2 are bf16 */
+#define MOE_WDTYPE_FP8_E4M3  1   /* w13/w2 are E4M3FN with 128x128 fp32 block scales */
+
+/* GEMM tile path (moe_forward_args.path) */
+#define MOE_PATH_AUTO        0   /* the planner decides from rows per expert */
+#define MOE_PATH_SMALL_M     1   /* weight-streaming path: few rows per expert (decode) */
+#define MOE_PATH_LARGE_M     2   /* LDS-tiled path: many rows per expert (prefill) */
+
+/* limits */
+#define MOE_MAX_EXPERTS      1024
+#define MOE_MAX_TOPK         64
+#define MOE_QUANT_GROUP      128  /* fp8 activation group and weight block edge */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+MOE_API const char* moe_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+MOE_API int moe_version(void);
+
+/*
+ * moe_route — router softmax with top-k and renormalised weights.
+ *
+ * P2 section 1.1: the layer receives topk_ids / topk_weights from the router,
+ * and its block-fp8 test builds the weights with a softmax over the selected
+ * experts.  For each token t the k largest logits are selected (a tie goes to
+ * the lower expert index; ids are written in descending-logit order), and
+ *   renormalize != 0: w_j = exp(l_j - l_max) / sum over the k selected
+ *                     (softmax -> top-k -> renormalise; the full softmax
+ *                     denominator cancels)
+ *   renormalize == 0: w_j = exp(l_j - l_max) / sum over all E experts
+ * computed in fp32.  Selection compares the fp32 logits exactly.
+ *
+ *   logits        device, fp32 [T, E]   (finite values; NaN gives an
+ *                                        unspecified selection)
+ *   topk_ids      device, int32 [T, topk]  (output)
+ *   topk_weights  device, fp32  [T, topk]  (output)
+ * Requires 1 <= E <= MOE_MAX_EXPERTS, 1 <= topk <= min(E, MOE_MAX_TOPK).
+ */
+MOE_API int moe_route(const float* logits, int32_t T, int32_t E, int32_t topk,
+                      int32_t renormalize, int32_t* topk_ids, float* topk_weights,
+                      hipStream_t stream);
+
+/*
+ * moe_align_capacity — length of sorted_token_ids for moe_align:
+ * T*topk + E*(block_m - 1), the padded row count when every expert wastes
+ * block_m - 1 rows.  Host only.  Returns a negative status on invalid
+ * arguments or when the capacity exceeds INT32_MAX.
+ */
+MOE_API int64_t moe_align_capacity(int32_t T, int32_t topk, int32_t E, int32_t block_m);
+
+/*
+ * moe_align — token-to-expert alignment into expert-sorted, block-padded
+ * order (P2 section 1.1: sorted_token_ids, num_tokens_post_padded, and the
+ * per-block expert of the block-sorted GEMM, where "GEMM fills padding
+ * inside active blocks").
+ *
+ * With flat slot ids f = t*topk + j, c_e = #{f : topk_ids[f] == e} and
+ * P_e = ceil(c_e / block_m) * block_m, o_e = sum_{e' < e} P_e':
+ *   sorted_token_ids[o_e + r] = the r-th smallest f routed to e (r < c_e);
+ *       padding slots o_e + c_e .. o_e + P_e - 1 and the tail
+ *       [o_E, capacity) hold the sentinel T*topk;
+ *   expert_ids[b] = e for blocks b in [o_e / block_m, (o_e + P_e) / block_m),
+ *       -1 for the blocks past o_E (experts with no rows get no block);
+ *   num_tokens_post_padded[0] = o_E;
+ *   inv[f] = position of f in sorted_token_ids, -1 for unrouted slots.
+ * Every element of every output is written, so the result is a pure
+ * function of the inputs (bit-exact and deterministic).
+ *
+ *   topk_ids                device, int32 [T, topk]
+ *   sorted_token_ids        device, int32 [moe_align_capacity(...)]  (output)
+ *   expert_ids              device, int32 [ceil(capacity / block_m)] (output)
+ *   num_tokens_post_padded  device, int32 [1]                         (output)
+ *   inv                     device, int32 [T*topk] or NULL            (output)
+ * Requires 1 <= E <= MOE_MAX_EXPERTS, 1 <= topk <= MOE_MAX_TOPK,
+ * 1 <= block_m <= 1024.
+ */
+MOE_API int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E,
+                      int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_padded, int32_t* inv, hipStream_t stream);
+
+/*
+ * moe_quant_act — dynamic fp8 quantisation of bf16 activations, one
+ * power-of-two scale per row and 128-column group (P2 section 1.2, the fused
+ * kernel's scale rule, applied to the layer input as in the block-fp8 path):
+ *   s = smallest power of two >= fl32(max(amax, 1e-10) * fl32(1/448)),
+ *   q = E4M3FN_RNE(clamp(x / s, -448, 448))   (x / s is exact).
+ *
+ *   x       device, bf16 [rows, cols]
+ *   codes   device, E4M3FN [rows, cols]            (output)
+ *   scales  device, fp32 [rows, cols / 128]        (output)
+ * Requires cols % 128 == 0.
+ */
+MOE_API int moe_quant_act(const void* x, int32_t rows, int32_t cols, uint8_t* codes,
+                          float* scales, hipStream_t stream);
+
+/* Arguments of moe_forward (the pages' `apply(x, w1, w2, topk_weights,
+ * topk_ids, activation=SiLU, expert_map=None,
+ * apply_router_weight_on_input=False)`, P2 section 1.1). */
+typedef struct moe_forward_args {
+    int32_t T;            /* tokens */
+    int32_t E;            /* experts */
+    int32_t H;            /* hidden size (GEMM1 K, GEMM2 N) */
+    int32_t I;            /* expert intermediate size (GEMM2 K) */
+    int32_t topk;         /* routed experts per token */
+    int32_t wdtype;       /* MOE_WDTYPE_* */
+    const void* x;        /* device bf16 [T, H] */
+    const void* w13;      /* device [E, 2I, H]: rows [0, I) gate, [I, 2I) up */
+    const float* w13_scale; /* device fp32 [E, 2I/128, H/128] (fp8 only, else NULL) */
+    const void* w2;       /* device [E, H, I] */
+    const float* w2_scale;  /* device fp32 [E, H/128, I/128] (fp8 only, else NULL) */
+    const int32_t* topk_ids;   /* device int32 [T, topk] */
+    const float* topk_weights; /* device fp32 [T, topk] */
+    void* out;            /* device bf16 [T, H] (output) */
+    int32_t path;         /* MOE_PATH_*; AUTO unless a test forces a path */
+    int32_t block_m;      /* rows per expert block; 0 lets the planner choose */
+} moe_forward_args;
+
+/* What moe_forward will do for a set of arguments (the test spy). */
+typedef struct moe_plan_info {
+    int32_t path;          /* MOE_PATH_SMALL_M or MOE_PATH_LARGE_M */
+    int32_t block_m;       /* rows per expert block */
+    int64_t capacity;      /* sorted rows incl. worst-case padding */
+    int32_t num_blocks;    /* ceil(capacity / block_m): GEMM grid rows */
+    int32_t gemm1_cols;    /* GEMM1 columns (of 2I) per workgroup */
+    int32_t gemm2_cols;    /* GEMM2 columns (of H) per workgroup */
+    int32_t reserved;
+    int64_t workspace_bytes;
+    /* byte offsets of the forward's intermediates inside the workspace */
+    int64_t off_sorted_ids, off_expert_ids, off_num_post_padded;
+    int64_t off_xq, off_xs, off_inter, off_inter_scale, off_y;
+} moe_plan_info;
+
+/* moe_plan — fill *out for these arguments (host only, no device work).
+ * Pointers in *a are not inspected.  Returns a status. */
+MOE_API int moe_plan(const moe_forward_args* a, moe_plan_info* out);
+
+/* moe_forward_workspace — workspace bytes moe_forward needs for these
+ * arguments (host only); negative status on invalid arguments. */
+MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
+
+/*
+ * moe_forward — the fused MoE layer on one GPU:
+ *   align (block_m from the plan) -> [fp8: quantise x per token and
+ *   128-group] -> GEMM1 h = W13[e] . x_t over expert-sorted rows with the
+ *   SiLU-mul epilogue a = bf16(bf16(silu(bf16 h_gate)) * bf16 h_up)
+ *   [fp8: + per-row 128-group pow2 scale and E4M3 codes], kept in sorted
+ *   order (P2 sections 1.1 and 1.2) -> GEMM2 y = tw * (W2[e] . a) with the
+ *   router weight applied in fp32 after the GEMM (P2 section 1.1) ->
+ *   out_t = bf16(sum_j y_{t,j}) summed in fp32 in slot order j = 0..topk-1
+ *   (the expert aggregation of P1, "Backend-Wechsel").
+ * fp8 weights arrive pre-quantised with their fp32 block scales; the library
+ * never quantises weights.
+ *
+ *   workspace  device buffer of at least moe_forward_workspace(a) bytes,
+ *              256-byte aligned; its contents on entry do not matter and on
+ *              exit hold the intermediates (layout in moe_plan_info).
+ * Limits: bf16 requires H % 64 == 0 and I % 64 == 0; fp8 requires
+ * H % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED).
+ */
+MOE_API int moe_forward(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * moe_forward_profiled — moe_forward that also records HIP events on the
+ * caller's stream around its stages, for timing each kernel where it runs:
+ * events[i] is recorded before stage i and events[MOE_NUM_STAGES] after the
+ * last one.  Stages: 0 align, 1 fp8 activation quantisation (empty for bf16),
+ * 2 GEMM1 + SiLU-mul epilogue, 3 GEMM2, 4 combine.  The events are created by
+ * the caller (hipEventCreate); n_events must be at least MOE_NUM_STAGES + 1.
+ * Same results and errors as moe_forward, plus MOE_ERR_INVALID_ARG for a
+ * missing event array.
+ */
+#define MOE_NUM_STAGES 5
+MOE_API int moe_forward_profiled(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
+                                 hipStream_t stream, hipEvent_t* events, int32_t n_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,56 @@
+// Router-weighted top-k combine (the "expert aggregation" step of P1, section
+// "Backend-Wechsel für FP8-Modelle"): out[t] = bf16( sum_j y[t*topk + j] ),
+// summed in fp32 in slot order j = 0..topk-1; slots whose id is outside
+// [0, E) were not routed and are skipped.  The down GEMM already applied the
+// router weight and wrote y by flat slot, so the k rows of a token are
+// contiguous and every access here is a coalesced 16-byte vector.
+// HBM-bound: topk*H*4 bytes read and H*2 written per token.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y,
+                                                          const int32_t* __restrict__ ids, int T,
+                                                          int topk, int E, int H,
+                                                          uint16_t* __restrict__ out) {
+    const int per_row = H / 8;
+    const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (i >= int64_t(T) * per_row) return;
+    const int t = int(i / per_row);
+    const int h = int(i - int64_t(t) * per_row) * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < topk; ++j) {
+        const int e = ids[int64_t(t) * topk + j];
+        if (e < 0 || e >= E) continue;
+        const float* row = y + (int64_t(t) * topk + j) * H + h;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(row);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(row + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[q] = __fadd_rn(acc[q], a[q]);
+            acc[4 + q] = __fadd_rn(acc[4 + q], b[q]);
+        }
+    }
+    i32x4 packed;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        packed[q] = int(uint32_t(f32_to_bf16_rne(acc[2 * q])) | (uint32_t(f32_to_bf16_rne(acc[2 * q + 1])) << 16));
+    *reinterpret_cast<i32x4*>(out + int64_t(t) * H + h) = packed;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y, const int32_t* ids, int T, int topk, int E, int H,
+                          uint16_t* out, hipStream_t s) {
+    const int64_t n = int64_t(T) * (H / 8);
+    const int64_t blocks = (n + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(combine_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, s, y, ids, T, topk, E,
+                       H, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

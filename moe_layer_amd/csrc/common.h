@@ -1,0 +1,151 @@
+// Shared device helpers and internal launcher declarations of libmoe_mi355x.
+// Everything here targets gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// vector types for MFMA operands and wide memory accesses
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;   // 16x16x32 / 32x32x16 bf16 operand
+typedef __attribute__((ext_vector_type(4))) float f32x4;     // 16x16 accumulator
+typedef __attribute__((ext_vector_type(16))) float f32x16;   // 32x32 accumulator
+typedef __attribute__((ext_vector_type(8))) int i32x8;       // 16x16x128 fp8 operand (32 bytes)
+typedef __attribute__((ext_vector_type(4))) int i32x4;       // 16-byte load
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;   // fp8 activation group / weight block edge
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(uint32_t(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (a bf16 is the upper half of an fp32
+// word: add half an ulp of the kept part, plus one if the kept part is odd).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16_rne(f)); }
+
+// fp32 -> OCP E4M3FN byte, round to nearest even.  The input must be finite
+// and within [-448, 448] (callers clamp first).  E4M3FN: exponent bias 7,
+// 3 fraction bits, subnormal quantum 2^-9 below 2^-6.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    float a = __builtin_fabsf(v);
+    uint32_t code;
+    if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+        code = uint32_t(__builtin_rintf(a * 512.0f));   // exact scaling, RNE
+    } else {
+        uint32_t ua = u & 0x7fffffffu;
+        uint32_t exp = (ua >> 23) - 127u + 7u;  // biased e4m3 exponent (1..15)
+        uint32_t mant = ua & 0x7fffffu;
+        uint32_t keep = mant >> 20;             // top 3 fraction bits
+        uint32_t rest = mant & 0xfffffu;        // 20 dropped bits
+        uint32_t up = (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
+        code = (exp << 3) + keep + up;          // carry into the exponent is correct
+    }
+    return code | sign;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
+    float a = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;
+    return (c & 0x80u) ? -a : a;
+}
+
+// Smallest power of two >= s for a positive normal fp32 s, exact.
+__device__ __forceinline__ float pow2_ceil(float s) {
+    uint32_t u = __float_as_uint(s);
+    if ((u & 0x7fffffu) == 0) return s;
+    return __uint_as_float(((u >> 23) + 1u) << 23);
+}
+
+// Group scale from the group's absolute maximum: the fp32 product
+// max(amax, 1e-10) * (1/448), rounded up to a power of two.
+__device__ __forceinline__ float fp8_group_scale(float amax) {
+    const float s_raw = __fmul_rn(fmaxf(amax, 1e-10f), 1.0f / 448.0f);
+    return pow2_ceil(s_raw);
+}
+
+// Quantise v with a power-of-two scale s: v / s is exact, clamp, RNE.
+__device__ __forceinline__ uint32_t fp8_quant(float v, float inv_s) {
+    float q = __fmul_rn(v, inv_s);             // inv_s is a power of two: exact
+    q = fminf(fmaxf(q, -448.0f), 448.0f);
+    return f32_to_e4m3_rne(q);
+}
+
+// SiLU-gated multiply with the fused kernel's rounding points:
+// g, u already bf16 values; silu rounded to bf16; product rounded to bf16.
+__device__ __forceinline__ float silu_mul_bf16(float g, float u) {
+    const float e = expf(-g);
+    const float s = round_bf16(__fdiv_rn(g, __fadd_rn(1.0f, e)));
+    return round_bf16(__fmul_rn(s, u));
+}
+
+// ---------------------------------------------------------------------------
+// wave helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_max_16(float v) {
+    // max over aligned groups of 16 lanes
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// internal launchers (each .hip file owns its kernels)
+// ---------------------------------------------------------------------------
+hipError_t launch_route(const float* logits, int T, int E, int topk, int renormalize,
+                        int32_t* ids, float* weights, hipStream_t s);
+
+hipError_t launch_align(const int32_t* ids, int T, int topk, int E, int block_m, int64_t cap,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, int32_t* inv,
+                        hipStream_t s);
+
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
+                            hipStream_t s);
+
+struct GemmArgs {
+    int T, E, H, I, topk, block_m, num_blocks;
+    const uint16_t* x;          // bf16 [T,H]
+    const uint8_t* xq;          // fp8 [T,H]
+    const float* xs;            // fp32 [T,H/128]
+    const void* w13;
+    const float* w13_scale;
+    const void* w2;
+    const float* w2_scale;
+    const float* topk_weights;  // [T*topk]
+    const int32_t* sorted_ids;  // [cap]
+    const int32_t* expert_ids;  // [num_blocks]
+    const int32_t* ntpp;        // [1]
+    void* inter;                // bf16 or fp8 [cap, I]
+    float* inter_scale;         // fp32 [cap, I/128]
+    float* y;                   // fp32 [T*topk, H]
+};
+
+hipError_t launch_gemm1_small(const GemmArgs& g, bool fp8, hipStream_t s);
+hipError_t launch_gemm2_small(const GemmArgs& g, bool fp8, hipStream_t s);
+hipError_t launch_gemm1_large(const GemmArgs& g, bool fp8, hipStream_t s);
+hipError_t launch_gemm2_large(const GemmArgs& g, bool fp8, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const int32_t* ids, int T, int topk, int E, int H,
+                          uint16_t* out, hipStream_t s);
+
+}  // namespace moe

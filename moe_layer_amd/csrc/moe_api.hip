@@ -1,0 +1,253 @@
+// C ABI of libmoe_mi355x: argument validation, planning and the launch
+// sequence of the fused MoE layer.  Declarations, argument meaning and error
+// behaviour are documented in include/moe.h.
+#include "../../include/moe.h"
+
+#include <climits>
+#include <cstddef>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kVersionMajor = 1;
+constexpr int kVersionMinor = 0;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Planner: rows per expert decide the block size and the tile path.
+struct Plan {
+    int path;
+    int block_m;
+    int64_t cap;
+    int num_blocks;
+    int gemm1_cols, gemm2_cols;
+    int64_t off_sorted, off_eids, off_ntpp, off_xq, off_xs, off_inter, off_inter_scale, off_y, total;
+};
+
+int validate_forward_scalars(const moe_forward_args* a) {
+    if (!a) return MOE_ERR_INVALID_ARG;
+    if (a->T < 0 || a->E < 1 || a->E > MOE_MAX_EXPERTS || a->topk < 1 || a->topk > MOE_MAX_TOPK ||
+        a->H <= 0 || a->I <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (a->wdtype != MOE_WDTYPE_BF16 && a->wdtype != MOE_WDTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+    if (a->path < MOE_PATH_AUTO || a->path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
+    if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64)
+        return MOE_ERR_UNSUPPORTED;
+    const int q = a->wdtype == MOE_WDTYPE_FP8_E4M3 ? MOE_QUANT_GROUP : 64;
+    if (a->H % q != 0 || a->I % q != 0) return MOE_ERR_UNSUPPORTED;
+    if (int64_t(a->T) * a->topk > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int make_plan(const moe_forward_args* a, Plan* p) {
+    int st = validate_forward_scalars(a);
+    if (st != MOE_OK) return st;
+    const int64_t R = int64_t(a->T) * a->topk;
+    const bool fp8 = a->wdtype == MOE_WDTYPE_FP8_E4M3;
+    p->path = a->path == MOE_PATH_AUTO ? MOE_PATH_SMALL_M : a->path;
+    if (p->path == MOE_PATH_LARGE_M) return MOE_ERR_UNSUPPORTED;
+    int bm = a->block_m;
+    if (bm == 0) {
+        const double rows_per_expert = double(R) / a->E;
+        bm = rows_per_expert <= 16.0 ? 16 : rows_per_expert <= 32.0 ? 32 : 64;
+    }
+    p->block_m = bm;
+    p->cap = R + int64_t(a->E) * (bm - 1);
+    if (p->cap > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    p->num_blocks = int((p->cap + bm - 1) / bm);
+    p->gemm1_cols = fp8 ? 128 : 64;
+    p->gemm2_cols = (fp8 || a->H % 128 == 0) ? 128 : 64;
+
+    const int64_t rows = int64_t(p->num_blocks) * bm;   // every row a block can touch
+    const int64_t es = fp8 ? 1 : 2;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) { const int64_t o = off; off = round_up(off + bytes, 256); return o; };
+    p->off_sorted = take(p->cap * 4);
+    p->off_eids = take(int64_t(p->num_blocks) * 4);
+    p->off_ntpp = take(4);
+    p->off_xq = fp8 ? take(int64_t(a->T) * a->H) : -1;
+    p->off_xs = fp8 ? take(int64_t(a->T) * (a->H / MOE_QUANT_GROUP) * 4) : -1;
+    p->off_inter = take(rows * a->I * es);
+    p->off_inter_scale = fp8 ? take(rows * (a->I / MOE_QUANT_GROUP) * 4) : -1;
+    p->off_y = take(R * a->H * 4);
+    p->total = off;
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+MOE_API const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or option";
+        case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+        case MOE_ERR_HIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+MOE_API int moe_version(void) { return (kVersionMajor << 16) | kVersionMinor; }
+
+MOE_API int moe_route(const float* logits, int32_t T, int32_t E, int32_t topk, int32_t renormalize,
+                      int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || topk < 1 || topk > E || topk > MOE_MAX_TOPK)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
+        !aligned(topk_weights, 4))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_route(logits, T, E, topk, renormalize, topk_ids, topk_weights, stream));
+}
+
+MOE_API int64_t moe_align_capacity(int32_t T, int32_t topk, int32_t E, int32_t block_m) {
+    if (T < 0 || topk < 1 || topk > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || block_m < 1 ||
+        block_m > 1024)
+        return MOE_ERR_INVALID_ARG;
+    const int64_t cap = int64_t(T) * topk + int64_t(E) * (block_m - 1);
+    if (cap > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    return cap;
+}
+
+MOE_API int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E, int32_t block_m,
+                      int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                      int32_t* inv, hipStream_t stream) {
+    const int64_t cap = moe_align_capacity(T, topk, E, block_m);
+    if (cap < 0) return int(cap);
+    if (!sorted_token_ids || !expert_ids || !num_tokens_post_padded || !aligned(sorted_token_ids, 4) ||
+        !aligned(expert_ids, 4) || !aligned(num_tokens_post_padded, 4) || (inv && !aligned(inv, 4)))
+        return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_ids || !aligned(topk_ids, 4))) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_align(topk_ids, T, topk, E, block_m, cap, sorted_token_ids, expert_ids,
+                                   num_tokens_post_padded, inv, stream));
+}
+
+MOE_API int moe_quant_act(const void* x, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
+                          hipStream_t stream) {
+    if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+    if (cols % MOE_QUANT_GROUP != 0) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_quant_act(static_cast<const uint16_t*>(x), rows, cols, codes, scales, stream));
+}
+
+MOE_API int moe_plan(const moe_forward_args* a, moe_plan_info* out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    Plan p;
+    const int st = make_plan(a, &p);
+    if (st != MOE_OK) return st;
+    out->path = p.path;
+    out->block_m = p.block_m;
+    out->capacity = p.cap;
+    out->num_blocks = p.num_blocks;
+    out->gemm1_cols = p.gemm1_cols;
+    out->gemm2_cols = p.gemm2_cols;
+    out->reserved = 0;
+    out->workspace_bytes = p.total;
+    out->off_sorted_ids = p.off_sorted;
+    out->off_expert_ids = p.off_eids;
+    out->off_num_post_padded = p.off_ntpp;
+    out->off_xq = p.off_xq;
+    out->off_xs = p.off_xs;
+    out->off_inter = p.off_inter;
+    out->off_inter_scale = p.off_inter_scale;
+    out->off_y = p.off_y;
+    return MOE_OK;
+}
+
+MOE_API int64_t moe_forward_workspace(const moe_forward_args* a) {
+    Plan p;
+    const int st = make_plan(a, &p);
+    return st != MOE_OK ? int64_t(st) : p.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                hipEvent_t* ev) {
+    Plan p;
+    int st = make_plan(a, &p);
+    if (st != MOE_OK) return st;
+    if (a->T == 0) return MOE_OK;
+    const bool fp8 = a->wdtype == MOE_WDTYPE_FP8_E4M3;
+    if (!a->x || !a->w13 || !a->w2 || !a->topk_ids || !a->topk_weights || !a->out ||
+        !aligned(a->x, 16) || !aligned(a->w13, 16) || !aligned(a->w2, 16) || !aligned(a->out, 16) ||
+        !aligned(a->topk_ids, 4) || !aligned(a->topk_weights, 4))
+        return MOE_ERR_INVALID_ARG;
+    if (fp8 && (!a->w13_scale || !a->w2_scale || !aligned(a->w13_scale, 4) || !aligned(a->w2_scale, 4)))
+        return MOE_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    GemmArgs g{};
+    g.T = a->T;
+    g.E = a->E;
+    g.H = a->H;
+    g.I = a->I;
+    g.topk = a->topk;
+    g.block_m = p.block_m;
+    g.num_blocks = p.num_blocks;
+    g.x = static_cast<const uint16_t*>(a->x);
+    g.xq = fp8 ? ws + p.off_xq : nullptr;
+    g.xs = fp8 ? reinterpret_cast<const float*>(ws + p.off_xs) : nullptr;
+    g.w13 = a->w13;
+    g.w13_scale = a->w13_scale;
+    g.w2 = a->w2;
+    g.w2_scale = a->w2_scale;
+    g.topk_weights = a->topk_weights;
+    g.sorted_ids = reinterpret_cast<const int32_t*>(ws + p.off_sorted);
+    g.expert_ids = reinterpret_cast<const int32_t*>(ws + p.off_eids);
+    g.ntpp = reinterpret_cast<const int32_t*>(ws + p.off_ntpp);
+    g.inter = ws + p.off_inter;
+    g.inter_scale = fp8 ? reinterpret_cast<float*>(ws + p.off_inter_scale) : nullptr;
+    g.y = reinterpret_cast<float*>(ws + p.off_y);
+
+    auto mark = [&](int i) { return ev ? hip_status(hipEventRecord(ev[i], stream)) : MOE_OK; };
+    if ((st = mark(0)) != MOE_OK) return st;
+    if ((st = hip_status(launch_align(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap,
+                                      reinterpret_cast<int32_t*>(ws + p.off_sorted),
+                                      reinterpret_cast<int32_t*>(ws + p.off_eids),
+                                      reinterpret_cast<int32_t*>(ws + p.off_ntpp), nullptr, stream))) != MOE_OK)
+        return st;
+    if ((st = mark(1)) != MOE_OK) return st;
+    if (fp8 && (st = hip_status(launch_quant_act(g.x, a->T, a->H, ws + p.off_xq,
+                                                 reinterpret_cast<float*>(ws + p.off_xs), stream))) != MOE_OK)
+        return st;
+    if ((st = mark(2)) != MOE_OK) return st;
+    if ((st = hip_status(launch_gemm1_small(g, fp8, stream))) != MOE_OK) return st;
+    if ((st = mark(3)) != MOE_OK) return st;
+    if ((st = hip_status(launch_gemm2_small(g, fp8, stream))) != MOE_OK) return st;
+    if ((st = mark(4)) != MOE_OK) return st;
+    if ((st = hip_status(launch_combine(g.y, a->topk_ids, a->T, a->topk, a->E, a->H,
+                                        static_cast<uint16_t*>(a->out), stream))) != MOE_OK)
+        return st;
+    return mark(5);
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API int moe_forward(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
+                        hipStream_t stream) {
+    return run_forward(a, workspace, workspace_bytes, stream, nullptr);
+}
+
+MOE_API int moe_forward_profiled(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
+                                 hipStream_t stream, hipEvent_t* events, int32_t n_events) {
+    if (!events || n_events < MOE_NUM_STAGES + 1) return MOE_ERR_INVALID_ARG;
+    return run_forward(a, workspace, workspace_bytes, stream, events);
+}
+
+}  // extern "C"

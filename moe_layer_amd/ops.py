@@ -1,0 +1,219 @@
+"""Python binding of libmoe_mi355x.so (include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  If the
+library is missing the first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+_lib = None
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_WDTYPE_BF16, MOE_WDTYPE_FP8_E4M3 = 0, 1
+MOE_PATH_AUTO, MOE_PATH_SMALL_M, MOE_PATH_LARGE_M = 0, 1, 2
+MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_QUANT_GROUP = 1024, 64, 128
+
+# every entry point include/moe.h declares
+EXPORTS = ("moe_status_string", "moe_version", "moe_route", "moe_align_capacity", "moe_align",
+           "moe_quant_act", "moe_plan", "moe_forward_workspace", "moe_forward", "moe_forward_profiled")
+MOE_NUM_STAGES = 5
+STAGE_NAMES = ("align", "quant_act", "gemm1", "gemm2", "combine")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+
+
+class ForwardArgs(C.Structure):
+    _fields_ = [("T", C.c_int32), ("E", C.c_int32), ("H", C.c_int32), ("I", C.c_int32),
+                ("topk", C.c_int32), ("wdtype", C.c_int32),
+                ("x", C.c_void_p), ("w13", C.c_void_p), ("w13_scale", C.c_void_p),
+                ("w2", C.c_void_p), ("w2_scale", C.c_void_p),
+                ("topk_ids", C.c_void_p), ("topk_weights", C.c_void_p), ("out", C.c_void_p),
+                ("path", C.c_int32), ("block_m", C.c_int32)]
+
+
+class PlanInfo(C.Structure):
+    _fields_ = [("path", C.c_int32), ("block_m", C.c_int32), ("capacity", C.c_int64),
+                ("num_blocks", C.c_int32), ("gemm1_cols", C.c_int32), ("gemm2_cols", C.c_int32),
+                ("reserved", C.c_int32), ("workspace_bytes", C.c_int64),
+                ("off_sorted_ids", C.c_int64), ("off_expert_ids", C.c_int64),
+                ("off_num_post_padded", C.c_int64), ("off_xq", C.c_int64), ("off_xs", C.c_int64),
+                ("off_inter", C.c_int64), ("off_inter_scale", C.c_int64), ("off_y", C.c_int64)]
+
+
+def lib() -> C.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m moe_layer_amd.build`")
+        L = C.CDLL(_LIB_PATH)
+        vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_status_string.argtypes = [C.c_int]
+        L.moe_version.restype = C.c_int
+        L.moe_route.restype = C.c_int
+        L.moe_route.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_align_capacity.restype = i64
+        L.moe_align_capacity.argtypes = [i32, i32, i32, i32]
+        L.moe_align.restype = C.c_int
+        L.moe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.moe_quant_act.restype = C.c_int
+        L.moe_quant_act.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_plan.restype = C.c_int
+        L.moe_plan.argtypes = [C.POINTER(ForwardArgs), C.POINTER(PlanInfo)]
+        L.moe_forward_workspace.restype = i64
+        L.moe_forward_workspace.argtypes = [C.POINTER(ForwardArgs)]
+        L.moe_forward.restype = C.c_int
+        L.moe_forward.argtypes = [C.POINTER(ForwardArgs), vp, i64, vp]
+        L.moe_forward_profiled.restype = C.c_int
+        L.moe_forward_profiled.argtypes = [C.POINTER(ForwardArgs), vp, i64, vp, C.POINTER(C.c_void_p), i32]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+moe_status_string = status_string
+
+
+def moe_version() -> int:
+    return lib().moe_version()
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def moe_route(logits: torch.Tensor, topk: int, renormalize: bool = True, topk_ids=None, topk_weights=None):
+    """Router softmax + top-k on fp32 logits [T, E]; returns (ids int32 [T,k], weights fp32 [T,k])."""
+    assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.dim() == 2
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    _check("moe_route", lib().moe_route(_ptr(logits), T, E, topk, int(bool(renormalize)), _ptr(topk_ids),
+                                        _ptr(topk_weights), _stream(logits.device)))
+    return topk_ids, topk_weights
+
+
+def moe_align_capacity(T: int, topk: int, E: int, block_m: int) -> int:
+    cap = lib().moe_align_capacity(T, topk, E, block_m)
+    if cap < 0:
+        raise MoeError("moe_align_capacity", int(cap))
+    return int(cap)
+
+
+def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, with_inv: bool = True):
+    """Expert-sorted, block-padded alignment of int32 ids [T, k]."""
+    assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous() and topk_ids.dim() == 2
+    T, k = topk_ids.shape
+    cap = moe_align_capacity(T, k, E, block_m)
+    dev = topk_ids.device
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(-(-cap // block_m), dtype=torch.int32, device=dev)
+    ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev) if with_inv else None
+    _check("moe_align", lib().moe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids), _ptr(expert_ids),
+                                        _ptr(ntpp), _ptr(inv), _stream(dev)))
+    return dict(sorted_token_ids=sorted_ids, expert_ids=expert_ids, num_tokens_post_padded=ntpp, inv=inv)
+
+
+def moe_quant_act(x: torch.Tensor):
+    """Per-row, per-128-column fp8 quantisation of bf16 x; returns (codes uint8, scales fp32)."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.dim() == 2
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, max(cols // MOE_QUANT_GROUP, 1)), dtype=torch.float32, device=x.device)
+    _check("moe_quant_act", lib().moe_quant_act(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(x.device)))
+    return codes, scales
+
+
+def _u8(t):
+    if t is None:
+        return None
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=None, out=None,
+                 path=MOE_PATH_AUTO, block_m=0, shape=None) -> ForwardArgs:
+    """Build the moe_forward_args struct.  With ``shape=(T, E, H, I, topk, wdtype)``
+    the tensors may be None (for planning and validation)."""
+    if shape is None:
+        T, H = x.shape
+        E, twoI, _ = w13.shape
+        topk = topk_ids.shape[1]
+        fp8 = w13.dtype in (torch.uint8, torch.float8_e4m3fn)
+        shape = (T, E, H, twoI // 2, topk, MOE_WDTYPE_FP8_E4M3 if fp8 else MOE_WDTYPE_BF16)
+    T, E, H, I, topk, wdtype = shape
+    a = ForwardArgs()
+    a.T, a.E, a.H, a.I, a.topk, a.wdtype = T, E, H, I, topk, wdtype
+    a.x, a.w13, a.w13_scale = _ptr(x), _ptr(_u8(w13)), _ptr(w13_scale)
+    a.w2, a.w2_scale = _ptr(_u8(w2)), _ptr(w2_scale)
+    a.topk_ids, a.topk_weights, a.out = _ptr(topk_ids), _ptr(topk_weights), _ptr(out)
+    a.path, a.block_m = path, block_m
+    return a
+
+
+def moe_plan(args: ForwardArgs) -> dict:
+    info = PlanInfo()
+    _check("moe_plan", lib().moe_plan(C.byref(args), C.byref(info)))
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+
+def moe_forward_workspace(args: ForwardArgs) -> int:
+    n = lib().moe_forward_workspace(C.byref(args))
+    if n < 0:
+        raise MoeError("moe_forward_workspace", int(n))
+    return int(n)
+
+
+def moe_forward(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=None, out=None,
+                workspace=None, path=MOE_PATH_AUTO, block_m=0):
+    """The fused MoE layer: bf16 x [T,H], w13 [E,2I,H], w2 [E,H,I] (bf16, or
+    e4m3 with fp32 128x128 block scales), int32 ids [T,k], fp32 weights [T,k].
+    Returns (out bf16 [T,H], workspace)."""
+    T, H = x.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out, path, block_m)
+    need = moe_forward_workspace(a)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check("moe_forward", lib().moe_forward(C.byref(a), _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out, workspace
+
+
+def moe_forward_profiled(args: ForwardArgs, workspace: torch.Tensor, events, stream=None):
+    """moe_forward on prepared args with HIP events recorded around its stages.
+    ``events``: MOE_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True) objects;
+    they are recorded on ``stream`` (default: the current stream), the stream
+    the kernels run on."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    for e in events:                      # make sure the underlying hipEvent_t exists
+        if e.cuda_event == 0:
+            e.record(s)
+    arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+    _check("moe_forward_profiled", lib().moe_forward_profiled(
+        C.byref(args), _ptr(workspace), workspace.numel(), C.c_void_p(s.cuda_stream), arr, len(events)))

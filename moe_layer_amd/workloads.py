@@ -180,13 +180,17 @@ class Workload:
     # -- expert weights ------------------------------------------------------
     def w13_f32(self, e: int) -> np.ndarray:
         c = self.cfg
-        w = _rng(c.seed, TID_W13, e).standard_normal((2 * c.I, c.H), dtype=np.float32)
-        return (w * np.float32(1.0 / math.sqrt(c.H))).astype(np.float32)
+        w = np.empty((2 * c.I, c.H), dtype=np.float32)
+        _rng(c.seed, TID_W13, e).standard_normal(out=w, dtype=np.float32)
+        w *= np.float32(1.0 / math.sqrt(c.H))
+        return w
 
     def w2_f32(self, e: int) -> np.ndarray:
         c = self.cfg
-        w = _rng(c.seed, TID_W2, e).standard_normal((c.H, c.I), dtype=np.float32)
-        return (w * np.float32(1.0 / math.sqrt(c.I))).astype(np.float32)
+        w = np.empty((c.H, c.I), dtype=np.float32)
+        _rng(c.seed, TID_W2, e).standard_normal(out=w, dtype=np.float32)
+        w *= np.float32(1.0 / math.sqrt(c.I))
+        return w
 
     def expert_weights(self, e: int):
         """Layer-format weights of expert e.

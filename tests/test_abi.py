@@ -1,0 +1,150 @@
+"""The C ABI on the host: every symbol include/moe.h declares is exported, and
+the host-only functions (capacity, planning, workspace, validation) behave as
+documented.  Every call here either is host-only or fails validation before
+any device work, so no GPU is needed."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from moe_layer_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = 0x7f0000000000          # 256-byte aligned address that is never dereferenced
+ODD = FAKE + 2                 # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+def test_header_declares_the_binding_exports():
+    assert sorted(declared_functions()) == sorted(ops.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ops.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ops._LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)$", out, re.M))
+    assert set(declared_functions()) == exported
+
+
+def test_version_and_status_strings():
+    assert ops.moe_version() >> 16 == 1
+    assert ops.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert ops.status_string(s) != "unknown status"
+    assert ops.status_string(123) == "unknown status"
+
+
+@pytest.mark.parametrize("T,k,E,B", [(3, 2, 3, 4), (16, 8, 128, 16), (4096, 8, 128, 64), (0, 8, 256, 16)])
+def test_align_capacity(T, k, E, B):
+    assert ops.moe_align_capacity(T, k, E, B) == T * k + E * (B - 1)
+
+
+def test_align_capacity_errors():
+    L = ops.lib()
+    assert L.moe_align_capacity(-1, 2, 3, 4) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align_capacity(3, 0, 3, 4) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align_capacity(3, 2, 0, 4) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align_capacity(3, 2, 1025, 4) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align_capacity(3, 2, 3, 0) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align_capacity(2 ** 28, 64, 1024, 1024) == ops.MOE_ERR_UNSUPPORTED
+
+
+def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAKE, scales=True):
+    a = ops.forward_args(None, None, None, None, None, shape=(T, E, H, I, k, wdtype), path=path, block_m=block_m)
+    for f in ("x", "w13", "w2", "topk_ids", "topk_weights", "out"):
+        setattr(a, f, ptr)
+    if wdtype == ops.MOE_WDTYPE_FP8_E4M3 and scales:
+        a.w13_scale = a.w2_scale = FAKE
+    return a
+
+
+@pytest.mark.parametrize("T,E,k,wdtype,expect_bm", [
+    (16, 128, 8, 0, 16),      # decode: 1 row per expert
+    (1024, 256, 8, 1, 32),    # fp8: 32 rows per expert
+    (64, 8, 2, 0, 16),        # tiny: 16 rows per expert
+    (4096, 128, 8, 0, 64),    # prefill: 256 rows per expert
+])
+def test_plan_block_size(T, E, k, wdtype, expect_bm):
+    H, I = (4096, 256) if wdtype else (4096, 1536)
+    p = ops.moe_plan(_args(T, E, H, I, k, wdtype))
+    assert p["block_m"] == expect_bm
+    assert p["capacity"] == T * k + E * (expect_bm - 1)
+    assert p["num_blocks"] == -(-p["capacity"] // expect_bm)
+    assert p["workspace_bytes"] == ops.moe_forward_workspace(_args(T, E, H, I, k, wdtype))
+    offs = [p[n] for n in ("off_sorted_ids", "off_expert_ids", "off_num_post_padded", "off_xq", "off_xs",
+                           "off_inter", "off_inter_scale", "off_y") if p[n] >= 0]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert p["off_y"] + T * k * H * 4 <= p["workspace_bytes"]
+    if wdtype:
+        assert p["off_xq"] >= 0 and p["off_inter_scale"] >= 0
+    else:
+        assert p["off_xq"] == -1 and p["off_inter_scale"] == -1
+
+
+def test_plan_block_override_and_path():
+    assert ops.moe_plan(_args(block_m=64))["block_m"] == 64
+    assert ops.moe_plan(_args(path=ops.MOE_PATH_SMALL_M))["path"] == ops.MOE_PATH_SMALL_M
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), ops.MOE_ERR_INVALID_ARG),
+    (dict(E=0), ops.MOE_ERR_INVALID_ARG),
+    (dict(E=1025), ops.MOE_ERR_INVALID_ARG),
+    (dict(k=0), ops.MOE_ERR_INVALID_ARG),
+    (dict(k=65), ops.MOE_ERR_INVALID_ARG),
+    (dict(H=0), ops.MOE_ERR_INVALID_ARG),
+    (dict(wdtype=7), ops.MOE_ERR_INVALID_ARG),
+    (dict(path=9), ops.MOE_ERR_INVALID_ARG),
+    (dict(block_m=48), ops.MOE_ERR_UNSUPPORTED),
+    (dict(H=4000), ops.MOE_ERR_UNSUPPORTED),                # bf16 needs H % 64 == 0
+    (dict(I=1500), ops.MOE_ERR_UNSUPPORTED),
+    (dict(H=4032, wdtype=1, I=256), ops.MOE_ERR_UNSUPPORTED),  # fp8 needs H % 128 == 0
+    (dict(I=192, wdtype=1), ops.MOE_ERR_UNSUPPORTED),
+    (dict(ptr=None), ops.MOE_ERR_INVALID_ARG),
+    (dict(ptr=ODD), ops.MOE_ERR_INVALID_ARG),
+    (dict(wdtype=1, I=256, scales=False), ops.MOE_ERR_INVALID_ARG),
+])
+def test_forward_validation(kw, status):
+    a = _args(**kw)
+    assert ops.lib().moe_forward(C.byref(a), C.c_void_p(FAKE), 1 << 40, None) == status
+
+
+def test_forward_workspace_errors():
+    a = _args()
+    need = ops.moe_forward_workspace(a)
+    L = ops.lib()
+    assert L.moe_forward(C.byref(a), C.c_void_p(FAKE), need - 1, None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_forward(C.byref(a), None, need, None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_forward(C.byref(a), C.c_void_p(FAKE + 16), need, None) == ops.MOE_ERR_WORKSPACE
+
+
+def test_forward_zero_tokens_is_a_noop():
+    a = _args(T=0, ptr=None)
+    assert ops.lib().moe_forward(C.byref(a), None, 0, None) == ops.MOE_OK
+
+
+def test_route_align_quant_validation():
+    L = ops.lib()
+    f = C.c_void_p(FAKE)
+    assert L.moe_route(f, 4, 8, 9, 1, f, f, None) == ops.MOE_ERR_INVALID_ARG       # topk > E
+    assert L.moe_route(f, 4, 0, 1, 1, f, f, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_route(f, 4, 2000, 8, 1, f, f, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_route(None, 4, 8, 2, 1, f, f, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_route(None, 0, 8, 2, 1, None, None, None) == ops.MOE_OK           # no tokens
+    assert L.moe_align(f, 4, 2, 8, 0, f, f, f, None, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align(f, 4, 2, 8, 16, None, f, f, None, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align(C.c_void_p(FAKE + 1), 4, 2, 8, 16, f, f, f, None, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_act(f, 4, 100, f, f, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_act(f, -1, 128, f, f, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_act(C.c_void_p(FAKE + 8), 4, 128, f, f, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_act(None, 0, 128, None, None, None) == ops.MOE_OK

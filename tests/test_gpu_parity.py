@@ -1,0 +1,255 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI.
+
+Routing ids, alignment buffers and fp8 activation codes/scales are compared
+bit-exactly; layer outputs with the rule in tests/gpu_util.py.  Workloads are
+the seeded configurations of moe_layer_amd.workloads (full sizes, with sampled
+oracle rows where the whole layer would take the oracle minutes), plus edge
+cases: ragged and tiny shapes, invalid and duplicate ids, empty experts.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from moe_layer_amd import ops
+from moe_layer_amd.workloads import CONFIGS, Workload
+
+from gpu_util import (TAU, bits_to_bf16, compare_output, dev, layer_for, log, oracle_tokens,
+                      route_weight_tol, routing, run_forward)
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------- routing ---
+
+def _check_route(lg: np.ndarray, k: int, renormalize=True):
+    lg_t = torch.from_numpy(lg).to(dev())
+    ids, w = ops.moe_route(lg_t, k, renormalize)
+    ids, w = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    ids_o, w_o = O.route(lg, k, renormalize)
+    np.testing.assert_array_equal(ids, ids_o)
+    assert np.all(np.abs(w - w_o) <= route_weight_tol(lg, ids_o, w_o)), np.max(np.abs(w - w_o) / w_o)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew"])
+def test_route_workloads(name):
+    cfg = CONFIGS[name]
+    log(f"route {name}")
+    _check_route(Workload(cfg).logits(), cfg.topk)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 7, 2), (257, 64, 8), (100, 65, 64), (33, 256, 8),
+                                   (17, 1024, 64), (5, 1000, 3)])
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_route_ties_and_shapes(T, E, k, renormalize):
+    rng = np.random.default_rng(T * E + k)
+    lg = rng.integers(-4, 5, size=(T, E)).astype(np.float32)          # heavy ties
+    _check_route(lg, k, renormalize)
+    lg = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    _check_route(lg, k, renormalize)
+
+
+# --------------------------------------------------------------- alignment ---
+
+def _check_align(ids: np.ndarray, E: int, B: int):
+    a = ops.moe_align(torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev()), E, B)
+    o = O.align(ids, E, B)
+    np.testing.assert_array_equal(a["sorted_token_ids"].cpu().numpy(), o["sorted_token_ids"])
+    np.testing.assert_array_equal(a["expert_ids"].cpu().numpy(), o["expert_ids"])
+    assert int(a["num_tokens_post_padded"].item()) == o["num_tokens_post_padded"]
+    np.testing.assert_array_equal(a["inv"].cpu().numpy(), o["inv"])
+
+
+@pytest.mark.parametrize("T,k,E,B", [(1, 1, 1, 1), (3, 2, 3, 4), (16, 8, 128, 16), (7, 3, 5, 64),
+                                     (1024, 8, 256, 32), (4096, 8, 128, 64), (999, 5, 1024, 16),
+                                     (50, 4, 9, 1024), (2000, 64, 40, 7)])
+def test_align_random_ids(T, k, E, B):
+    rng = np.random.default_rng(T + E + B)
+    ids = rng.integers(-2, E + 2, size=(T, k))      # invalid ids and duplicates included
+    _check_align(ids, E, B)
+
+
+@pytest.mark.parametrize("name,B", [("decode", 16), ("prefill", 64), ("fp8", 32), ("skew", 64), ("skew", 16)])
+def test_align_workloads(name, B):
+    cfg = CONFIGS[name]
+    ids, _, _ = routing(cfg)
+    _check_align(ids, cfg.E, B)
+
+
+def test_align_empty_experts_worked_example():
+    _check_align(np.array([[3, 1], [1, 3]]), 4, 2)
+
+
+# ------------------------------------------------------ fp8 activation quant ---
+
+def test_quant_act_bit_exact():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal((300, 1024)) * 0.1).astype(np.float32)
+    x[0] = 0.0                                   # all-zero rows: scale from the 1e-10 floor
+    x[1] *= 1e-6                                 # e4m3 subnormal codes
+    x[2] *= 1e4
+    x[3, :128] = 1.75                            # the amax=1.75 boundary case
+    x[4, ::2] = -x[4, ::2]
+    x = np.concatenate([x, Workload(CONFIGS["fp8"]).x_f32()[:64, :1024]])
+    bits = torch.from_numpy(x).to(torch.bfloat16)
+    codes, scales = ops.moe_quant_act(bits.to(dev()))
+    xo = bits.to(torch.float64).numpy()
+    c_o, s_o, _ = O.quant_act(xo)
+    np.testing.assert_array_equal(scales.cpu().numpy().astype(np.float64), s_o)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_o)
+
+
+# ----------------------------------------------------------------- forward ---
+
+def _forward_case(cfg, tokens=None, **kw):
+    """Run route (if the workload routes from logits) + forward on the GPU and
+    compare with the oracle on ``tokens`` (all when None)."""
+    wl = Workload(cfg)
+    ids_o, tw_o, lg = routing(cfg)
+    if lg is not None:
+        ids_t, tw_t = ops.moe_route(torch.from_numpy(lg).to(dev()), cfg.topk)
+        ids = ids_t.cpu().numpy()
+        np.testing.assert_array_equal(ids, ids_o)
+        tw32 = tw_t.cpu().numpy()
+    else:
+        ids, tw32 = ids_o, tw_o.astype(np.float32)
+    layer = layer_for(cfg)
+    layer.ensure(np.unique(ids))
+    log(f"forward {cfg.name} T={cfg.T} {cfg.wdtype} {kw}")
+    out, ws, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw32, **kw)
+    gpu = out.to(torch.float64).cpu().numpy()
+    tokens = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
+    o = oracle_tokens(layer, wl.x_exact(), ids_o, tw_o, tokens)
+    excess, raw, floor = compare_output(gpu[tokens], o)
+    log(f"  excess/RMS={excess:.3e} raw max/RMS={raw:.3e} bf16 floor/RMS={floor:.3e}")
+    assert np.all(np.isfinite(gpu))
+    assert excess <= TAU[cfg.wdtype], (excess, raw)
+    return out, ws
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_m", [0, 16, 32, 64])
+def test_forward_tiny(wdtype, block_m):
+    _forward_case(replace(CONFIGS["tiny"], wdtype=wdtype), block_m=block_m)
+
+
+def test_forward_decode():
+    _forward_case(CONFIGS["decode"])
+
+
+def test_forward_fp8_workload():
+    _forward_case(CONFIGS["fp8"])
+
+
+def test_forward_prefill_sampled():
+    rng = np.random.default_rng(1)
+    _forward_case(CONFIGS["prefill"], tokens=np.sort(rng.choice(4096, 192, replace=False)))
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 64])
+def test_forward_skew_small_batches(T):
+    _forward_case(CONFIGS["skew"].with_tokens(T))
+
+
+def test_forward_skew_full_sampled():
+    rng = np.random.default_rng(2)
+    _forward_case(CONFIGS["skew"], tokens=np.sort(rng.choice(8192, 64, replace=False)))
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+def test_forward_ragged_shapes(wdtype):
+    """Odd token counts, an expert count that is not a power of two, H/I at the
+    smallest supported multiples, invalid and duplicate ids."""
+    from moe_layer_amd.workloads import Config
+    q = 128 if wdtype == "fp8" else 64
+    cfg = Config("ragged", 37, 13, 3 * q, 5 * q if wdtype == "bf16" else 2 * q, 3, wdtype, "given")
+    wl = Workload(cfg)
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, 13, size=(37, 3)).astype(np.int32)
+    ids[0, 1] = ids[0, 0]        # duplicate
+    ids[1, 2] = -1               # not routed
+    ids[2, 0] = 13               # not routed
+    ids[3:6] = 4                 # three duplicates
+    tw = rng.random((37, 3)).astype(np.float32)
+    layer = layer_for(cfg)
+    layer.ensure(range(13))
+    for bm in (16, 32, 64):
+        out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=bm)
+        gpu = out.to(torch.float64).cpu().numpy()
+        o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(37))
+        excess, raw, _ = compare_output(gpu, o)
+        log(f"ragged {wdtype} bm={bm}: excess/RMS={excess:.3e} raw={raw:.3e}")
+        assert excess <= TAU[wdtype]
+
+
+# ------------------------------------------------------ self-consistency ---
+
+def _layer_inputs(cfg):
+    wl = Workload(cfg)
+    ids, tw, lg = routing(cfg)
+    layer = layer_for(cfg)
+    layer.ensure(np.unique(ids))
+    return wl, layer, ids.astype(np.int32), tw.astype(np.float32)
+
+
+@pytest.mark.parametrize("name,wdtype", [("tiny", "bf16"), ("tiny", "fp8"), ("decode", "bf16"), ("fp8", "fp8")])
+def test_block_m_invariance_bitwise(name, wdtype):
+    """Every output element is accumulated over K in the same order whatever the
+    block size, so the output is bit-identical across block_m."""
+    cfg = replace(CONFIGS[name], wdtype=wdtype)
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    ref = None
+    for bm in (16, 32, 64):
+        out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=bm)
+        if ref is None:
+            ref = out.clone()
+        else:
+            assert torch.equal(out, ref), f"block_m={bm}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "fp8"])
+def test_token_permutation_equivariance(name):
+    cfg = CONFIGS[name]
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    x = wl.x_bf16_bits()
+    p = np.random.default_rng(3).permutation(cfg.T)
+    out, _, _ = run_forward(layer, x, ids, tw)
+    outp, _, _ = run_forward(layer, x[p], ids[p], tw[p])
+    assert torch.equal(outp, out[torch.from_numpy(p).to(out.device)])
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "fp8"])
+def test_determinism_and_poisoned_workspace(name):
+    """Two runs agree bitwise, also when the workspace starts as all-NaN bytes:
+    no padding row or unwritten workspace value reaches the output."""
+    cfg = CONFIGS[name]
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    out1, ws, (x, ids_t, tw_t) = run_forward(layer, wl.x_bf16_bits(), ids, tw)
+    ws.fill_(0xFF)
+    out2, _ = ops.moe_forward(x, layer.w13, layer.w2, ids_t, tw_t, layer.s13, layer.s2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+
+
+def test_output_guard_bands():
+    cfg = CONFIGS["tiny"]
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    T, H = cfg.T, cfg.H
+    buf = torch.full((T + 8, H), 7.0, dtype=torch.bfloat16, device=dev())
+    x = bits_to_bf16(wl.x_bf16_bits()).to(dev())
+    ids_t = torch.from_numpy(ids).to(dev())
+    tw_t = torch.from_numpy(tw).to(dev())
+    ops.moe_forward(x, layer.w13, layer.w2, ids_t, tw_t, out=buf[4:4 + T])
+    torch.cuda.synchronize()
+    assert torch.all(buf[:4] == 7.0) and torch.all(buf[4 + T:] == 7.0)
+    ref, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw)
+    assert torch.equal(buf[4:4 + T], ref)
+
+
+def test_plan_reports_the_path_taken():
+    cfg = CONFIGS["decode"]
+    a = ops.forward_args(None, None, None, None, None, shape=(cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk, 0))
+    p = ops.moe_plan(a)
+    assert p["path"] == ops.MOE_PATH_SMALL_M and p["block_m"] == 16
