@@ -164,7 +164,8 @@ typedef struct moe_forward_args {
     const float* topk_weights; /* device fp32 [T, topk] */
     void* out;            /* device bf16 [T, H] (output) */
     int32_t path;         /* MOE_PATH_*; AUTO unless a test forces a path */
-    int32_t block_m;      /* rows per expert block; 0 lets the planner choose */
+    int32_t block_m;      /* rows per expert block; 0 lets the planner choose;
+                             small-M path: 16, 32 or 64; large-M path: 128 */
 } moe_forward_args;
 
 /* What moe_forward will do for a set of arguments (the test spy). */
@@ -173,8 +174,8 @@ typedef struct moe_plan_info {
     int32_t block_m;       /* rows per expert block */
     int64_t capacity;      /* sorted rows incl. worst-case padding */
     int32_t num_blocks;    /* ceil(capacity / block_m): GEMM grid rows */
-    int32_t gemm1_cols;    /* GEMM1 columns (of 2I) per workgroup */
-    int32_t gemm2_cols;    /* GEMM2 columns (of H) per workgroup */
+    int32_t gemm1_cols;    /* GEMM1 weight rows (of 2I, gate + up) per workgroup */
+    int32_t gemm2_cols;    /* GEMM2 weight rows (of H) per workgroup */
     int32_t reserved;
     int64_t workspace_bytes;
     /* byte offsets of the forward's intermediates inside the workspace */
@@ -207,7 +208,9 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  *              256-byte aligned; its contents on entry do not matter and on
  *              exit hold the intermediates (layout in moe_plan_info).
  * Limits: bf16 requires H % 64 == 0 and I % 64 == 0; fp8 requires
- * H % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED).
+ * H % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED).  The large-M
+ * path needs bf16 weights, H % 256 == 0 and I % 128 == 0; AUTO takes it from
+ * 96 routed rows per expert on, forcing it elsewhere is MOE_ERR_UNSUPPORTED.
  */
 MOE_API int moe_forward(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
                         hipStream_t stream);

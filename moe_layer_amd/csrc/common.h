@@ -144,6 +144,8 @@ hipError_t launch_gemm1_small(const GemmArgs& g, bool fp8, hipStream_t s);
 hipError_t launch_gemm2_small(const GemmArgs& g, bool fp8, hipStream_t s);
 hipError_t launch_gemm1_large(const GemmArgs& g, bool fp8, hipStream_t s);
 hipError_t launch_gemm2_large(const GemmArgs& g, bool fp8, hipStream_t s);
+bool gemm_large_supported(int H, int I, bool fp8);   // shapes the LDS-tiled path handles
+int gemm_large_block_m();                            // its rows per expert block
 
 hipError_t launch_combine(const float* y, const int32_t* ids, int T, int topk, int E, int H,
                           uint16_t* out, hipStream_t s);

@@ -14,6 +14,8 @@ namespace {
 
 constexpr int kVersionMajor = 1;
 constexpr int kVersionMinor = 0;
+// rows per expert from which the LDS-tiled path beats weight streaming
+constexpr double kLargeMinRowsPerExpert = 96.0;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -35,7 +37,7 @@ int validate_forward_scalars(const moe_forward_args* a) {
         return MOE_ERR_INVALID_ARG;
     if (a->wdtype != MOE_WDTYPE_BF16 && a->wdtype != MOE_WDTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
     if (a->path < MOE_PATH_AUTO || a->path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
-    if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64)
+    if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128)
         return MOE_ERR_UNSUPPORTED;
     const int q = a->wdtype == MOE_WDTYPE_FP8_E4M3 ? MOE_QUANT_GROUP : 64;
     if (a->H % q != 0 || a->I % q != 0) return MOE_ERR_UNSUPPORTED;
@@ -48,19 +50,32 @@ int make_plan(const moe_forward_args* a, Plan* p) {
     if (st != MOE_OK) return st;
     const int64_t R = int64_t(a->T) * a->topk;
     const bool fp8 = a->wdtype == MOE_WDTYPE_FP8_E4M3;
-    p->path = a->path == MOE_PATH_AUTO ? MOE_PATH_SMALL_M : a->path;
-    if (p->path == MOE_PATH_LARGE_M) return MOE_ERR_UNSUPPORTED;
+    const double rows_per_expert = double(R) / a->E;
+    const bool large_ok = gemm_large_supported(a->H, a->I, fp8);
+    int path = a->path;
+    if (path == MOE_PATH_AUTO) path = (large_ok && rows_per_expert >= kLargeMinRowsPerExpert) ? MOE_PATH_LARGE_M
+                                                                                              : MOE_PATH_SMALL_M;
     int bm = a->block_m;
-    if (bm == 0) {
-        const double rows_per_expert = double(R) / a->E;
-        bm = rows_per_expert <= 16.0 ? 16 : rows_per_expert <= 32.0 ? 32 : 64;
+    if (path == MOE_PATH_LARGE_M) {
+        if (!large_ok) return MOE_ERR_UNSUPPORTED;
+        if (bm == 0) bm = gemm_large_block_m();
+        if (bm != gemm_large_block_m()) return MOE_ERR_UNSUPPORTED;
+    } else {
+        if (bm == 0) bm = rows_per_expert <= 16.0 ? 16 : rows_per_expert <= 32.0 ? 32 : 64;
+        if (bm > 64) return MOE_ERR_UNSUPPORTED;
     }
+    p->path = path;
     p->block_m = bm;
     p->cap = R + int64_t(a->E) * (bm - 1);
     if (p->cap > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     p->num_blocks = int((p->cap + bm - 1) / bm);
-    p->gemm1_cols = fp8 ? 128 : 64;
-    p->gemm2_cols = (fp8 || a->H % 128 == 0) ? 128 : 64;
+    if (path == MOE_PATH_LARGE_M) {
+        p->gemm1_cols = 256;   // 128 gate + 128 up rows
+        p->gemm2_cols = 256;
+    } else {
+        p->gemm1_cols = fp8 ? 256 : 128;   // gate + up rows per workgroup
+        p->gemm2_cols = (fp8 || a->H % 128 == 0) ? 128 : 64;
+    }
 
     const int64_t rows = int64_t(p->num_blocks) * bm;   // every row a block can touch
     const int64_t es = fp8 ? 1 : 2;
@@ -225,9 +240,12 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
                                                  reinterpret_cast<float*>(ws + p.off_xs), stream))) != MOE_OK)
         return st;
     if ((st = mark(2)) != MOE_OK) return st;
-    if ((st = hip_status(launch_gemm1_small(g, fp8, stream))) != MOE_OK) return st;
+    const bool large = p.path == MOE_PATH_LARGE_M;
+    if ((st = hip_status(large ? launch_gemm1_large(g, fp8, stream) : launch_gemm1_small(g, fp8, stream))) != MOE_OK)
+        return st;
     if ((st = mark(3)) != MOE_OK) return st;
-    if ((st = hip_status(launch_gemm2_small(g, fp8, stream))) != MOE_OK) return st;
+    if ((st = hip_status(large ? launch_gemm2_large(g, fp8, stream) : launch_gemm2_small(g, fp8, stream))) != MOE_OK)
+        return st;
     if ((st = mark(4)) != MOE_OK) return st;
     if ((st = hip_status(launch_combine(g.y, a->topk_ids, a->T, a->topk, a->E, a->H,
                                         static_cast<uint16_t*>(a->out), stream))) != MOE_OK)

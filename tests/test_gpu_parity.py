@@ -158,6 +158,47 @@ def test_forward_skew_full_sampled():
     _forward_case(CONFIGS["skew"], tokens=np.sort(rng.choice(8192, 64, replace=False)))
 
 
+def test_forward_tiny_large_path():
+    _forward_case(CONFIGS["tiny"], path=ops.MOE_PATH_LARGE_M)
+
+
+def test_forward_ragged_large_path():
+    """The LDS-tiled path on an odd token count, E not a power of two, blocks
+    whose last 32-row sub-tiles are partly or wholly padding, invalid and
+    duplicate ids."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config("ragged_large", 301, 5, 512, 384, 3, "bf16", "given")
+    wl = Workload(cfg)
+    rng = np.random.default_rng(6)
+    ids = rng.integers(0, 5, size=(301, 3)).astype(np.int32)
+    ids[0, 1] = ids[0, 0]
+    ids[1, 2] = -1
+    ids[2, 0] = 5
+    ids[10:200, 0] = 3                      # one hot expert with several full blocks
+    tw = rng.random((301, 3)).astype(np.float32)
+    layer = layer_for(cfg)
+    layer.ensure(range(5))
+    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_LARGE_M)
+    gpu = out.to(torch.float64).cpu().numpy()
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(301))
+    excess, raw, _ = compare_output(gpu, o)
+    log(f"ragged large: excess/RMS={excess:.3e} raw={raw:.3e}")
+    assert excess <= TAU["bf16"]
+
+
+def test_prefill_takes_the_large_path():
+    cfg = CONFIGS["prefill"]
+    a = ops.forward_args(None, None, None, None, None, shape=(cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk, 0))
+    p = ops.moe_plan(a)
+    assert p["path"] == ops.MOE_PATH_LARGE_M and p["block_m"] == 128
+
+
+def test_forward_prefill_small_path_sampled():
+    rng = np.random.default_rng(7)
+    _forward_case(CONFIGS["prefill"], tokens=np.sort(rng.choice(4096, 64, replace=False)),
+                  path=ops.MOE_PATH_SMALL_M)
+
+
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
 def test_forward_ragged_shapes(wdtype):
     """Odd token counts, an expert count that is not a power of two, H/I at the
@@ -220,7 +261,7 @@ def test_token_permutation_equivariance(name):
     assert torch.equal(outp, out[torch.from_numpy(p).to(out.device)])
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "fp8", "prefill"])
 def test_determinism_and_poisoned_workspace(name):
     """Two runs agree bitwise, also when the workspace starts as all-NaN bytes:
     no padding row or unwritten workspace value reaches the output."""
