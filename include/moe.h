@@ -165,7 +165,7 @@ typedef struct moe_forward_args {
     void* out;            /* device bf16 [T, H] (output) */
     int32_t path;         /* MOE_PATH_*; AUTO unless a test forces a path */
     int32_t block_m;      /* rows per expert block; 0 lets the planner choose;
-                             small-M path: 16, 32 or 64; large-M path: 128 */
+                             small-M path: 16, 32 or 64; large-M path: 256 */
 } moe_forward_args;
 
 /* What moe_forward will do for a set of arguments (the test spy). */

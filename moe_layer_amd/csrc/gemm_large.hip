@@ -2,27 +2,34 @@
 //
 // Same orientation as the weight-streaming path: the expert's weight rows are
 // the MFMA M side, the block's tokens the N side (so the GEMM1 epilogue keeps a
-// gate row and its up row in the same lane and register).  A workgroup owns a
-// 256-weight-row x 128-token tile of one expert block and walks K in stages of
-// 64: each stage of both operands (256x64 and 128x64 bf16) is loaded from
-// global memory into registers one stage ahead, then written to one of two LDS
-// buffers, so one barrier per stage separates the writers from the readers.
-// LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-// position c ^ (r & 7), so the 32 lanes of an MFMA fragment read that walk 32
-// consecutive rows hit different banks.
+// gate row and its up row in the same lane and register).  A workgroup of 8
+// waves owns a 256-weight-row x 256-token tile of one expert block: wave
+// (wm, wn) = (w & 3, w >> 2) owns weight rows 64wm..64wm+63 and the token
+// sub-tiles u (32 rows each) with u % 2 == wn, so the live sub-tiles of a
+// block's partly filled tail split evenly between the two waves of a SIMD.
+// K is walked in stages of 64: both operand tiles of the next stage (256x64
+// bf16 each, 64 KiB) are loaded into registers while the current stage is
+// multiplied from LDS, then written to the other of two LDS buffers; one
+// barrier per stage (32 MFMAs per wave).  Every LDS access is ordinary code,
+// so the compiler interleaves the fragment reads with the MFMAs.
+//
+// LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r sits at
+// position c ^ ((r >> 1) & 7), which spreads the 32 rows a fragment read
+// touches evenly over the banks (for 32 and for 64 four-byte banks).
 //
 // MFMA v_mfma_f32_32x32x16_bf16 (layout checked on gfx950): lane l holds row
 // (l % 32) of A / column (l % 32) of B at K offset (l / 32) * 8; the 32x32
 // result gives lane l column (l % 32) and rows (i / 4) * 8 + (l / 32) * 4 + i % 4.
 //
-// Token sub-tiles of 32 rows that hold only padding (the tail of an expert's
-// last block) are neither loaded nor multiplied.
+// Token sub-tiles that hold only padding (the tail of an expert's last block)
+// are neither multiplied nor stored: the main loop is instantiated per wave for
+// 0..4 live sub-tiles.
 //
 //   GEMM1 (a4+a5): tile = 128 intermediate columns: gate rows c0..c0+127 and
-//                  up rows I+c0..; wave w owns gate rows c0+32w.. and the
-//                  matching up rows; epilogue a = bf16(bf16(silu(bf16 g)) *
+//                  up rows I+c0..; wave (wm, .) owns gate rows c0+32wm.. and
+//                  the matching up rows; epilogue a = bf16(bf16(silu(bf16 g)) *
 //                  bf16 u) stored in expert-sorted order (P2 sections 1.1, 1.2).
-//   GEMM2 (a6):    tile = 256 output columns h; wave w owns h0+64w..+63;
+//   GEMM2 (a6):    tile = 256 output columns h; wave (wm, .) owns h0+64wm..;
 //                  epilogue y[f] = tw[f] * acc in fp32 (P2 section 1.1).
 #include "common.h"
 
@@ -31,21 +38,23 @@ namespace moe {
 namespace {
 
 constexpr int kTM = 256;           // weight rows per workgroup
-constexpr int kBM = 128;           // tokens per workgroup (= block_m of the alignment)
+constexpr int kBM = 256;           // tokens per workgroup (= block_m of the alignment)
 constexpr int kKB = 64;            // K per stage (bf16 elements)
 constexpr int kRowBytes = kKB * 2; // 128 bytes per LDS row
-constexpr int kThreads = 256;
-constexpr int kABytes = kTM * kRowBytes;   // 32 KiB
-constexpr int kBBytes = kBM * kRowBytes;   // 16 KiB
-constexpr int kALoads = kABytes / 16 / kThreads;   // 8 x 16 B per thread per stage
-constexpr int kBLoads = kBBytes / 16 / kThreads;   // 4 x 16 B per thread per stage
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileBytes = 256 * kRowBytes;         // one operand stage: 32 KiB
+constexpr int kStageBytes = 2 * kTileBytes;         // weights + tokens
+constexpr int kLoads = kTileBytes / 16 / kThreads;  // 16-byte loads per thread per operand (4)
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ bool map_tile(int num_blocks, int ntiles, int& blk, int& tile) {
     // hardware deals workgroups round-robin over the 8 XCDs; give each XCD a
     // contiguous run of logical tiles, ordered tile-major so the blocks of one
-    // expert (same weight tile) run together on one XCD and share its L2
+    // expert (same weight tile) run together on one XCD and share its L2 (a
+    // block-major order, which shares the token rows instead, measured slower
+    // on every workload)
     const int per_xcd = gridDim.x >> 3;
     const int wg = blockIdx.x;
     const int logical = (wg & 7) * per_xcd + (wg >> 3);
@@ -55,147 +64,108 @@ __device__ __forceinline__ bool map_tile(int num_blocks, int ntiles, int& blk, i
     return true;
 }
 
-template <int GEMM>
-__global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int ntiles) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kABytes + kBBytes];
-    __shared__ int s_valid;
-
-    int blk, tile;
-    if (!map_tile(g.num_blocks, ntiles, blk, tile)) return;
-    const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
-    if (e < 0) return;
-
+template <int GEMM, int NU>
+__device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int blk, int tile, int e) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
+    const int wm = wv & 3, wn = wv >> 2;
     const int R = g.T * g.topk;
     const int K = GEMM == 1 ? g.H : g.I;
     const int nst = K / kKB;
+    const int64_t kbytes = int64_t(K) * 2;
 
-    // rows of this block that hold real slots (a prefix: padding sits at the end)
-    if (tid < 64) {
-        const int f0 = g.sorted_ids[blk * kBM + tid];
-        const int f1 = g.sorted_ids[blk * kBM + 64 + tid];
-        const int n = __popcll(__ballot(f0 < R)) + __popcll(__ballot(f1 < R));
-        if (tid == 0) s_valid = n;
-    }
-    __syncthreads();
-    const int nvalid = s_valid;
-    const int ntok_tiles = (nvalid + 31) >> 5;   // 32-token sub-tiles with real rows
-
-    // ---- global source pointers --------------------------------------------
-    // A: thread tid loads chunk (tid & 7) of rows j*32 + tid/8, j = 0..7
-    const int a_chunk = tid & 7;
-    const int a_row0 = tid >> 3;
-    const uint8_t* a_src[kALoads];
-    {
-        const uint8_t* w = static_cast<const uint8_t*>(GEMM == 1 ? g.w13 : g.w2);
+    // ---- global sources: thread tid moves chunk (tid & 7) of rows j*64 + tid/8 --
+    const int chunk = tid & 7;
+    const int row0 = tid >> 3;   // 0..63
+    const uint8_t* a_src[kLoads];
+    const uint8_t* b_src[kLoads];
 #pragma unroll
-        for (int j = 0; j < kALoads; ++j) {
-            const int r = j * 32 + a_row0;   // tile row 0..255
-            int grow;
-            if (GEMM == 1) {
-                // rows 0..127 gate c0+r, 128..255 up I+c0+r-128; wave w reads gate rows
-                // [32w, 32w+32) at tile rows [64w, 64w+32) and up rows at [64w+32, 64w+64)
-                const int ww = r >> 6, half = (r >> 5) & 1, rr = r & 31;
-                const int col = tile * 128 + ww * 32 + rr;
-                grow = half ? g.I + col : col;
-                grow += e * 2 * g.I;
-            } else {
-                grow = e * g.H + tile * kTM + r;
-            }
-            a_src[j] = w + int64_t(grow) * K * 2 + a_chunk * 16;
-        }
-    }
-    const uint8_t* b_src[kBLoads];
-    bool b_on[kBLoads];
-#pragma unroll
-    for (int j = 0; j < kBLoads; ++j) {
-        const int r = j * 32 + a_row0;   // token row 0..127
-        b_on[j] = r < ntok_tiles * 32;
-        const int srow = blk * kBM + r;
-        if (GEMM == 1) {
-            const int f = g.sorted_ids[srow];
-            const int tok = f < R ? f / g.topk : 0;
-            b_src[j] = reinterpret_cast<const uint8_t*>(g.x) + int64_t(tok) * K * 2 + a_chunk * 16;
+    for (int j = 0; j < kLoads; ++j) {
+        const int r = j * 64 + row0;   // tile row 0..255
+        if constexpr (GEMM == 1) {
+            // tile row r = 64w + 32*half + rr: weight-wave w's gate rows, then its up rows
+            const int half = (r >> 5) & 1, rr = r & 31;
+            const int64_t grow = int64_t(e) * 2 * g.I + (half ? g.I : 0) + tile * 128 + (r >> 6) * 32 + rr;
+            a_src[j] = static_cast<const uint8_t*>(g.w13) + grow * kbytes + chunk * 16;
+            const int f = g.sorted_ids[blk * kBM + r];
+            const int tok = f < R ? f / g.topk : 0;   // padding rows read token 0 (never stored as real rows)
+            b_src[j] = reinterpret_cast<const uint8_t*>(g.x) + int64_t(tok) * kbytes + chunk * 16;
         } else {
-            b_src[j] = static_cast<const uint8_t*>(g.inter) + int64_t(srow) * K * 2 + a_chunk * 16;
+            const int64_t grow = int64_t(e) * g.H + tile * kTM + r;
+            a_src[j] = static_cast<const uint8_t*>(g.w2) + grow * kbytes + chunk * 16;
+            b_src[j] = static_cast<const uint8_t*>(g.inter) + int64_t(blk * kBM + r) * kbytes + chunk * 16;
         }
     }
-
-    i32x4 ra[kALoads], rb[kBLoads];
+    i32x4 ra[kLoads], rb[kLoads];
     auto gload = [&](int st) {
         const int64_t off = int64_t(st) * kRowBytes;
 #pragma unroll
-        for (int j = 0; j < kALoads; ++j) ra[j] = *reinterpret_cast<const i32x4*>(a_src[j] + off);
-#pragma unroll
-        for (int j = 0; j < kBLoads; ++j)
-            if (b_on[j]) rb[j] = *reinterpret_cast<const i32x4*>(b_src[j] + off);
+        for (int j = 0; j < kLoads; ++j) {
+            ra[j] = *reinterpret_cast<const i32x4*>(a_src[j] + off);
+            rb[j] = *reinterpret_cast<const i32x4*>(b_src[j] + off);
+        }
     };
     auto lstore = [&](int buf) {
-        uint8_t* A = lds[buf];
-        uint8_t* B = lds[buf] + kABytes;
+        uint8_t* A = lds + buf * kStageBytes;
+        uint8_t* B = A + kTileBytes;
 #pragma unroll
-        for (int j = 0; j < kALoads; ++j)
-            *reinterpret_cast<i32x4*>(A + swz(j * 32 + a_row0, a_chunk)) = ra[j];
-#pragma unroll
-        for (int j = 0; j < kBLoads; ++j)
-            if (b_on[j]) *reinterpret_cast<i32x4*>(B + swz(j * 32 + a_row0, a_chunk)) = rb[j];
+        for (int j = 0; j < kLoads; ++j) {
+            *reinterpret_cast<i32x4*>(A + swz(j * 64 + row0, chunk)) = ra[j];
+            *reinterpret_cast<i32x4*>(B + swz(j * 64 + row0, chunk)) = rb[j];
+        }
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[2][NU > 0 ? NU : 1];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < (NU > 0 ? NU : 1); ++u)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[t][u][i] = 0.0f;
 
     const int fr = lane & 31;   // fragment row / column
     const int fk = lane >> 5;   // fragment K half
-    const int arow0 = wv * 64 + fr;
+    const int arow = wm * 64 + fr;
 
     gload(0);
     lstore(0);
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
         const int buf = st & 1;
-        if (st + 1 < nst) gload(st + 1);
-        const uint8_t* A = lds[buf];
-        const uint8_t* B = lds[buf] + kABytes;
+        const bool more = st + 1 < nst;
+        if (more) gload(st + 1);
+        const uint8_t* A = lds + buf * kStageBytes;
+        const uint8_t* B = A + kTileBytes;
 #pragma unroll
         for (int s = 0; s < kKB / 16; ++s) {
-            const int chunk = 2 * s + fk;
-            bf16x8 af[2], bfr[4];
+            const int c = 2 * s + fk;
+            i32x4 af[2], bf[NU > 0 ? NU : 1];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                af[t] = *reinterpret_cast<const bf16x8*>(A + swz(arow0 + t * 32, chunk));
+            for (int t = 0; t < 2; ++t) af[t] = *reinterpret_cast<const i32x4*>(A + swz(arow + t * 32, c));
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                bfr[u] = *reinterpret_cast<const bf16x8*>(B + swz(u * 32 + fr, chunk));
+            for (int u = 0; u < NU; ++u) bf[u] = *reinterpret_cast<const i32x4*>(B + swz((2 * u + wn) * 32 + fr, c));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (u < ntok_tiles) {
+            for (int u = 0; u < NU; ++u)
 #pragma unroll
-                    for (int t = 0; t < 2; ++t)
-                        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t], bfr[u], acc[t][u], 0, 0, 0);
-                }
-            }
+                for (int t = 0; t < 2; ++t)
+                    acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[t]),
+                                                                        __builtin_bit_cast(bf16x8, bf[u]),
+                                                                        acc[t][u], 0, 0, 0);
         }
-        if (st + 1 < nst) {
+        if (more) {
             lstore(buf ^ 1);
             __syncthreads();
         }
     }
 
-    // ---- epilogues -----------------------------------------------------------
+    // ---- epilogues: wave sub-tile u sits at token rows (2u + wn) * 32 ---------
     if constexpr (GEMM == 1) {
         uint16_t* out = static_cast<uint16_t*>(g.inter);
-        const int colw = tile * 128 + wv * 32;
+        const int colw = tile * 128 + wm * 32;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (u >= ntok_tiles) continue;
-            const int row = blk * kBM + u * 32 + fr;
+        for (int u = 0; u < NU; ++u) {
+            const int row = blk * kBM + (2 * u + wn) * 32 + fr;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {   // groups of 4 consecutive columns
                 uint32_t p[2];
@@ -211,11 +181,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
             }
         }
     } else {
-        const int hw = tile * kTM + wv * 64;
+        const int hw = tile * kTM + wm * 64;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (u >= ntok_tiles) continue;
-            const int f = g.sorted_ids[blk * kBM + u * 32 + fr];
+        for (int u = 0; u < NU; ++u) {
+            const int f = g.sorted_ids[blk * kBM + (2 * u + wn) * 32 + fr];
             if (f >= R) continue;
             const float tw = g.topk_weights[f];
             float* yrow = g.y + int64_t(f) * g.H;
@@ -229,6 +198,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
                     *reinterpret_cast<f32x4*>(yrow + hw + t * 32 + q * 8 + fk * 4) = v;
                 }
         }
+    }
+}
+
+template <int GEMM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int ntiles) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+    __shared__ int s_valid;
+
+    int blk, tile;
+    if (!map_tile(g.num_blocks, ntiles, blk, tile)) return;
+    const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
+    if (e < 0) return;
+
+    // rows of this block that hold real slots (a prefix: padding sits at the end)
+    const int R = g.T * g.topk;
+    if (threadIdx.x < 64) {
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < kBM / 64; ++q) n += __popcll(__ballot(g.sorted_ids[blk * kBM + q * 64 + threadIdx.x] < R));
+        if (threadIdx.x == 0) s_valid = n;
+    }
+    __syncthreads();
+    // live 32-token sub-tiles of this wave: u = wn, wn + 2, ... below the count
+    const int live = (s_valid + 31) >> 5;
+    const int wn = (threadIdx.x >> 6) >> 2;
+    switch ((live - wn + 1) >> 1) {
+        case 0: run_tile<GEMM, 0>(g, lds, blk, tile, e); break;
+        case 1: run_tile<GEMM, 1>(g, lds, blk, tile, e); break;
+        case 2: run_tile<GEMM, 2>(g, lds, blk, tile, e); break;
+        case 3: run_tile<GEMM, 3>(g, lds, blk, tile, e); break;
+        default: run_tile<GEMM, 4>(g, lds, blk, tile, e); break;
     }
 }
 

@@ -125,7 +125,8 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&ap)[MT], const u
 // Workgroup -> (block, column tile).  The hardware deals workgroups to the 8
 // XCDs round-robin; remap so each XCD walks a contiguous run of logical tiles,
 // and order logical tiles column-tile-major so consecutive blocks of one
-// expert (same weights) run on the same XCD and share its L2.
+// expert (same weights) run on the same XCD and share its L2 (block-major
+// order, sharing token rows instead, measured slower on every workload).
 __device__ __forceinline__ bool map_tile(int num_blocks, int ntiles, int& blk, int& tile) {
     const int per_xcd = gridDim.x >> 3;   // grid is a multiple of 8
     const int wg = blockIdx.x;

@@ -37,7 +37,7 @@ int validate_forward_scalars(const moe_forward_args* a) {
         return MOE_ERR_INVALID_ARG;
     if (a->wdtype != MOE_WDTYPE_BF16 && a->wdtype != MOE_WDTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
     if (a->path < MOE_PATH_AUTO || a->path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
-    if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128)
+    if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 256)
         return MOE_ERR_UNSUPPORTED;
     const int q = a->wdtype == MOE_WDTYPE_FP8_E4M3 ? MOE_QUANT_GROUP : 64;
     if (a->H % q != 0 || a->I % q != 0) return MOE_ERR_UNSUPPORTED;

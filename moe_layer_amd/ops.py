@@ -11,7 +11,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+# MOE_MI355X_LIB points the binding at another build of the same library
+_LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libmoe_mi355x.so")
 _lib = None
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4

@@ -73,7 +73,7 @@ def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAK
     (1024, 256, 8, 1, 32, ops.MOE_PATH_SMALL_M),    # fp8: 32 rows per expert
     (64, 8, 2, 0, 16, ops.MOE_PATH_SMALL_M),        # tiny: 16 rows per expert
     (512, 64, 8, 0, 64, ops.MOE_PATH_SMALL_M),      # 64 rows per expert
-    (4096, 128, 8, 0, 128, ops.MOE_PATH_LARGE_M),   # prefill: 256 rows per expert
+    (4096, 128, 8, 0, 256, ops.MOE_PATH_LARGE_M),   # prefill: 256 rows per expert
 ])
 def test_plan_block_size(T, E, k, wdtype, expect_bm, expect_path):
     H, I = (4096, 256) if wdtype else (4096, 1536)
@@ -97,7 +97,7 @@ def test_plan_block_override_and_path():
     assert ops.moe_plan(_args(block_m=64))["block_m"] == 64
     assert ops.moe_plan(_args(path=ops.MOE_PATH_SMALL_M))["path"] == ops.MOE_PATH_SMALL_M
     p = ops.moe_plan(_args(path=ops.MOE_PATH_LARGE_M))
-    assert p["path"] == ops.MOE_PATH_LARGE_M and p["block_m"] == 128
+    assert p["path"] == ops.MOE_PATH_LARGE_M and p["block_m"] == 256
     # prefill-sized layer forced onto the weight-streaming path
     p = ops.moe_plan(_args(T=4096, path=ops.MOE_PATH_SMALL_M))
     assert p["path"] == ops.MOE_PATH_SMALL_M and p["block_m"] == 64
@@ -112,7 +112,8 @@ def test_plan_large_path_limits():
     assert L.moe_plan(C.byref(_args(T=4096, H=4160, path=ops.MOE_PATH_LARGE_M)), C.byref(info)) \
         == ops.MOE_ERR_UNSUPPORTED
     assert L.moe_plan(C.byref(_args(path=ops.MOE_PATH_LARGE_M, block_m=64)), C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
-    assert L.moe_plan(C.byref(_args(path=ops.MOE_PATH_SMALL_M, block_m=128)), C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_plan(C.byref(_args(path=ops.MOE_PATH_SMALL_M, block_m=256)), C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_plan(C.byref(_args(block_m=128)), C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
     # AUTO falls back to the weight-streaming path where the large one cannot run
     assert ops.moe_plan(_args(T=4096, H=4160))["path"] == ops.MOE_PATH_SMALL_M
     assert ops.moe_plan(_args(T=8192, wdtype=1, I=256))["path"] == ops.MOE_PATH_SMALL_M

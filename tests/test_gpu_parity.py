@@ -190,7 +190,7 @@ def test_prefill_takes_the_large_path():
     cfg = CONFIGS["prefill"]
     a = ops.forward_args(None, None, None, None, None, shape=(cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk, 0))
     p = ops.moe_plan(a)
-    assert p["path"] == ops.MOE_PATH_LARGE_M and p["block_m"] == 128
+    assert p["path"] == ops.MOE_PATH_LARGE_M and p["block_m"] == 256
 
 
 def test_forward_prefill_small_path_sampled():
