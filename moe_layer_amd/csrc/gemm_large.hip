@@ -49,21 +49,6 @@ constexpr int kLoads = kTileBytes / 16 / kThreads;  // 16-byte loads per thread 
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-__device__ __forceinline__ bool map_tile(int num_blocks, int ntiles, int& blk, int& tile) {
-    // hardware deals workgroups round-robin over the 8 XCDs; give each XCD a
-    // contiguous run of logical tiles, ordered tile-major so the blocks of one
-    // expert (same weight tile) run together on one XCD and share its L2 (a
-    // block-major order, which shares the token rows instead, measured slower
-    // on every workload)
-    const int per_xcd = gridDim.x >> 3;
-    const int wg = blockIdx.x;
-    const int logical = (wg & 7) * per_xcd + (wg >> 3);
-    if (logical >= num_blocks * ntiles) return false;
-    tile = logical / num_blocks;
-    blk = logical - tile * num_blocks;
-    return true;
-}
-
 template <int GEMM, int NU>
 __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int blk, int tile, int e) {
     const int tid = threadIdx.x;
@@ -207,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
     __shared__ int s_valid;
 
     int blk, tile;
-    if (!map_tile(g.num_blocks, ntiles, blk, tile)) return;
+    if (!map_active_tile(g, ntiles, blk, tile)) return;
     const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
     if (e < 0) return;
 

@@ -37,6 +37,20 @@ struct Op {
 
 __device__ __forceinline__ i32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const i32x4*>(p); }
 
+// A read-only load through the scalar data cache: p must be uniform over the
+// wave (built from kernel arguments, block and wave indices), so the value
+// lands in a scalar register and costs no vector memory instruction.
+__device__ __forceinline__ float ld_uniform(const float* p) {
+    return *(const __attribute__((address_space(4))) float*)p;
+}
+
+// fp8 activation group scales are staged per workgroup in LDS, kTabSteps
+// K-blocks at a time: one vector load per (token, group) per workgroup
+// instead of one per (token, group) per wave.  Row stride padded by one word
+// so the 16 rows of a tile read distinct banks.
+constexpr int kTabSteps = 64;
+constexpr int kTabStride = kTabSteps + 1;
+
 template <bool FP8>
 __device__ __forceinline__ f32x4 mfma(const i32x4 (&a)[2], const i32x4 (&b)[2], f32x4 c) {
     if constexpr (FP8) {
@@ -78,9 +92,9 @@ __device__ __forceinline__ void load_stage(Stage<FP8, MT, NT, U>& st, const uint
             for (int p = 0; p < O::kParts; ++p) st.b[u][n][p] = ld16(bp[n] + off + 16 * p);
         if constexpr (FP8) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m) st.sa[u][m] = asp[m][step0 + u];
+            for (int m = 0; m < MT; ++m) st.sa[u][m] = ld_uniform(asp[m] + step0 + u);   // weight block
 #pragma unroll
-            for (int n = 0; n < NT; ++n) st.sb[u][n] = bsp[n][step0 + u];
+            for (int n = 0; n < NT; ++n) st.sb[u][n] = bsp[n][step0 + u];                // LDS table
         }
     }
 }
@@ -106,7 +120,12 @@ __device__ __forceinline__ void compute_stage(const Stage<FP8, MT, NT, U>& st, f
             }
 }
 
-// K loop over nsteps MFMA steps (nsteps % U == 0), two stages in flight.
+// K loop over nsteps MFMA steps (nsteps % U == 0): load the next stage, then
+// compute the current one.  The loads sit under a branch, so the compiler
+// waits for all of them before each compute: one stage is in flight per wave,
+// and HBM latency is hidden by many waves per CU (the tiles are sized for
+// occupancy).  Deeper software pipelines (3-4 stages with scheduling
+// barriers) cost occupancy and measured slower on every decode shape.
 template <bool FP8, int MT, int NT, int U>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&ap)[MT], const uint8_t* const (&bp)[NT],
                                          const float* const (&asp)[MT], const float* const (&bsp)[NT],
@@ -122,19 +141,39 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&ap)[MT], const u
     }
 }
 
-// Workgroup -> (block, column tile).  The hardware deals workgroups to the 8
-// XCDs round-robin; remap so each XCD walks a contiguous run of logical tiles,
-// and order logical tiles column-tile-major so consecutive blocks of one
-// expert (same weights) run on the same XCD and share its L2 (block-major
-// order, sharing token rows instead, measured slower on every workload).
-__device__ __forceinline__ bool map_tile(int num_blocks, int ntiles, int& blk, int& tile) {
-    const int per_xcd = gridDim.x >> 3;   // grid is a multiple of 8
-    const int wg = blockIdx.x;
-    const int logical = (wg & 7) * per_xcd + (wg >> 3);
-    if (logical >= num_blocks * ntiles) return false;
-    tile = logical / num_blocks;
-    blk = logical - tile * num_blocks;
-    return true;
+// fp8 K loop: per chunk of kTabSteps K-blocks, stage the BM rows' activation
+// scales (row_scale(r) points at row r's first group) in LDS, then run the
+// mainloop over the chunk.  Every thread of the workgroup takes part.
+template <int MT, int NT, int BM, int NTHREADS, typename RowScale>
+__device__ __forceinline__ void mainloop_fp8(const uint8_t* const (&ap)[MT], const uint8_t* const (&bp)[NT],
+                                             const float* const (&asp)[MT], RowScale row_scale, int nsteps,
+                                             float* tab, f32x4 (&acc)[MT][NT]) {
+    using O = Op<true>;
+    const int lr = threadIdx.x & 15;
+    for (int c0 = 0; c0 < nsteps; c0 += kTabSteps) {
+        const int cs = min(kTabSteps, nsteps - c0);
+        __syncthreads();   // the previous chunk's table reads are done
+        for (int i = threadIdx.x; i < BM * cs; i += NTHREADS) {
+            const int r = i / cs, k = i - r * cs;
+            tab[r * kTabStride + k] = row_scale(r)[c0 + k];
+        }
+        __syncthreads();
+        const uint8_t* apc[MT];
+        const float* aspc[MT];
+        const uint8_t* bpc[NT];
+        const float* bspc[NT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            apc[m] = ap[m] + int64_t(c0) * O::kStepBytes;
+            aspc[m] = asp[m] + c0;
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            bpc[n] = bp[n] + int64_t(c0) * O::kStepBytes;
+            bspc[n] = tab + (n * 16 + lr) * kTabStride;
+        }
+        mainloop<true, MT, NT, 1>(apc, bpc, aspc, bspc, cs, acc);
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -149,12 +188,12 @@ __global__ __launch_bounds__(NW * 64) void gemm1_small_kernel(GemmArgs g, int nt
     constexpr int BM = 16 * NT;
     constexpr int COLS = NW * WT * 16;   // intermediate columns per workgroup
     int blk, tile;
-    if (!map_tile(g.num_blocks, ntiles, blk, tile)) return;
+    if (!map_active_tile(g, ntiles, blk, tile)) return;
     const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
     if (e < 0) return;
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lk = lane >> 4;
     const int H = g.H, I = g.I, R = g.T * g.topk;
     const int i0 = tile * COLS + wv * WT * 16;   // first gate column of this wave
@@ -177,7 +216,7 @@ __global__ __launch_bounds__(NW * 64) void gemm1_small_kernel(GemmArgs g, int nt
         const int f = g.sorted_ids[blk * BM + n * 16 + lr];
         const int tok = f < R ? f / g.topk : 0;   // padding rows read token 0, never stored as real rows
         bp[n] = xs + int64_t(tok) * H * O::kElem + lk * O::kLaneOff;
-        bsp[n] = FP8 ? g.xs + int64_t(tok) * kb_count : nullptr;
+        bsp[n] = nullptr;
     }
 
     f32x4 acc[MT][NT];
@@ -185,7 +224,17 @@ __global__ __launch_bounds__(NW * 64) void gemm1_small_kernel(GemmArgs g, int nt
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
-    mainloop<FP8, MT, NT, U>(ap, bp, asp, bsp, H / O::kStepK, acc);
+    if constexpr (FP8) {
+        __shared__ float tab[BM * kTabStride];
+        const int32_t* rows = g.sorted_ids + blk * BM;
+        auto row_scale = [&](int r) {
+            const int f = rows[r];
+            return g.xs + int64_t(f < R ? f / g.topk : 0) * kb_count;
+        };
+        mainloop_fp8<MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, H / O::kStepK, tab, acc);
+    } else {
+        mainloop<FP8, MT, NT, U>(ap, bp, asp, bsp, H / O::kStepK, acc);
+    }
 
     // epilogue: a = silu(g) * u with the bf16 rounding points
     float a[WT][NT][4];
@@ -258,12 +307,12 @@ __global__ __launch_bounds__(NW * 64) void gemm2_small_kernel(GemmArgs g, int nt
     constexpr int BM = 16 * NT;
     constexpr int COLS = NW * WT * 16;
     int blk, tile;
-    if (!map_tile(g.num_blocks, ntiles, blk, tile)) return;
+    if (!map_active_tile(g, ntiles, blk, tile)) return;
     const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
     if (e < 0) return;
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lk = lane >> 4;
     const int H = g.H, I = g.I, R = g.T * g.topk;
     const int h0 = tile * COLS + wv * WT * 16;
@@ -285,7 +334,7 @@ __global__ __launch_bounds__(NW * 64) void gemm2_small_kernel(GemmArgs g, int nt
     for (int n = 0; n < NT; ++n) {
         const int row = blk * BM + n * 16 + lr;
         bp[n] = inter + int64_t(row) * I * O::kElem + lk * O::kLaneOff;
-        bsp[n] = FP8 ? g.inter_scale + int64_t(row) * kb_count : nullptr;
+        bsp[n] = nullptr;
     }
 
     f32x4 acc[MT][NT];
@@ -293,7 +342,14 @@ __global__ __launch_bounds__(NW * 64) void gemm2_small_kernel(GemmArgs g, int nt
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
-    mainloop<FP8, MT, NT, U>(ap, bp, asp, bsp, I / O::kStepK, acc);
+    if constexpr (FP8) {
+        __shared__ float tab[BM * kTabStride];
+        const float* scales = g.inter_scale + int64_t(blk) * BM * kb_count;
+        auto row_scale = [&](int r) { return scales + int64_t(r) * kb_count; };
+        mainloop_fp8<MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, I / O::kStepK, tab, acc);
+    } else {
+        mainloop<FP8, MT, NT, U>(ap, bp, asp, bsp, I / O::kStepK, acc);
+    }
 
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -322,35 +378,46 @@ hipError_t launch_tiles(K kernel, const GemmArgs& g, int ntiles, int threads, hi
 template <bool FP8, int NT>
 hipError_t gemm1_dispatch(const GemmArgs& g, hipStream_t s) {
     if constexpr (FP8) {
-        constexpr int WT = 2, NW = 4;   // 4 waves x (32 gate + 32 up) = one 128-column group
-        return launch_tiles(gemm1_small_kernel<true, NT, WT, NW, 1>, g, g.I / (NW * WT * 16), NW * 64, s);
+        // one 128-column group per workgroup: 4 waves x (32 gate + 32 up)
+        // rows, or 8 waves x (16 + 16) for 64-token blocks (registers)
+        const int ntiles = g.I / 128;
+        if constexpr (NT <= 2) return launch_tiles(gemm1_small_kernel<true, NT, 2, 4, 1>, g, ntiles, 256, s);
+        else return launch_tiles(gemm1_small_kernel<true, NT, 1, 8, 1>, g, ntiles, 512, s);
     } else {
-        constexpr int WT = 1, NW = 4;   // 4 waves x (16 gate + 16 up) = 64 columns
-        const int nsteps = g.H / 32;
-        if (nsteps % 4 == 0)
-            return launch_tiles(gemm1_small_kernel<false, NT, WT, NW, 4>, g, g.I / (NW * WT * 16), NW * 64, s);
-        return launch_tiles(gemm1_small_kernel<false, NT, WT, NW, 2>, g, g.I / (NW * WT * 16), NW * 64, s);
+        // 4 waves x (16 gate + 16 up) = 64 columns
+        const int ntiles = g.I / 64;
+        if ((g.H / 32) % 4 == 0) return launch_tiles(gemm1_small_kernel<false, NT, 1, 4, 4>, g, ntiles, 256, s);
+        return launch_tiles(gemm1_small_kernel<false, NT, 1, 4, 2>, g, ntiles, 256, s);
     }
 }
 
-template <bool FP8, int NT, int WT>
+template <int NT, int WT>
 hipError_t gemm2_bf16(const GemmArgs& g, hipStream_t s) {
     constexpr int NW = 4;
-    const int nsteps = g.I / 32;
-    if (nsteps % 4 == 0)
+    if ((g.I / 32) % 4 == 0)
         return launch_tiles(gemm2_small_kernel<false, NT, WT, NW, 4>, g, g.H / (NW * WT * 16), NW * 64, s);
     return launch_tiles(gemm2_small_kernel<false, NT, WT, NW, 2>, g, g.H / (NW * WT * 16), NW * 64, s);
+}
+
+template <int NT, int WT>
+hipError_t gemm2_fp8(const GemmArgs& g, hipStream_t s) {
+    constexpr int NW = 4;
+    return launch_tiles(gemm2_small_kernel<true, NT, WT, NW, 1>, g, g.H / (NW * WT * 16), NW * 64, s);
 }
 
 template <bool FP8, int NT>
 hipError_t gemm2_dispatch(const GemmArgs& g, hipStream_t s) {
     if constexpr (FP8) {
-        constexpr int WT = 2, NW = 4;   // 4 waves x 32 output columns = 128
-        return launch_tiles(gemm2_small_kernel<true, NT, WT, NW, 1>, g, g.H / (NW * WT * 16), NW * 64, s);
+        // K = I is short: 64 output rows per wave keep more bytes in flight
+        // (32 for 64-token blocks, registers; 32 when H % 256 != 0)
+        if constexpr (NT <= 2) {
+            if (g.H % 256 == 0) return gemm2_fp8<NT, 4>(g, s);
+        }
+        return gemm2_fp8<NT, 2>(g, s);
     } else {
         // 128 output columns per workgroup, or 64 when H is not a multiple of 128
-        if (g.H % 128 == 0) return gemm2_bf16<false, NT, 2>(g, s);
-        return gemm2_bf16<false, NT, 1>(g, s);
+        if (g.H % 128 == 0) return gemm2_bf16<NT, 2>(g, s);
+        return gemm2_bf16<NT, 1>(g, s);
     }
 }
 

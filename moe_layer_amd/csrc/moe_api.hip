@@ -1,7 +1,7 @@
 // C ABI of libmoe_mi355x: argument validation, planning and the launch
 // sequence of the fused MoE layer.  Declarations, argument meaning and error
 // behaviour are documented in include/moe.h.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <climits>
 #include <cstddef>
