@@ -1,19 +1,22 @@
 // Token-to-expert alignment (P2 section 1.1: sorted_token_ids,
 // num_tokens_post_padded and the per-block expert of the block-sorted GEMM).
 //
-// One workgroup of 16 waves.  The flat slots f = t*topk + j are cut into 16
-// contiguous chunks, one per wave, and every wave walks its chunk 64 slots at
-// a time in ascending order.  A ballot multisplit (one ballot per bit of the
+// Flat slots f = t*topk + j are cut into chunks that waves walk 64 slots at a
+// time in ascending order.  A ballot multisplit (one ballot per bit of the
 // expert id) gives each lane the mask of lanes holding the same expert, so
-// ranks inside a 64-slot batch need no atomics:
-//   phase 1  per-wave expert counts cnt[w][e]
-//   phase 2  padded sizes, exclusive scan over experts, per-(wave, expert)
-//            start positions; padding slots of each expert get the sentinel
-//   phase 3  stable scatter: position = start[w][e] + rank inside the batch
-//   phase 4  tail of sorted_token_ids and expert_ids of every block
-// The output is a pure function of the input: rows of one expert appear in
-// ascending flat order because waves own ascending chunks and batches are
-// walked in order.
+// ranks inside a 64-slot batch need no atomics.  Rows of one expert end up in
+// ascending flat order because chunks are ascending and batches are walked in
+// order: the output is a pure function of the input.
+//
+// Two forms with the same output:
+//   align_kernel         one workgroup of 16 waves (no scratch memory):
+//                        per-wave counts, scan, stable scatter, tail
+//   align_count_kernel   many workgroups of 4 waves x 256 slots: per-
+//   align_scan_kernel    workgroup counts to scratch; one workgroup scans
+//   align_scatter_kernel them into per-workgroup start positions, padding,
+//                        tail and block experts; many workgroups scatter.
+//                        Used when the slot count is large enough that one
+//                        CU's ALUs would be the bottleneck.
 #include "common.h"
 
 namespace moe {
@@ -166,6 +169,192 @@ __global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restri
     }
 }
 
+// ---------------------------------------------------------------------------
+// multi-workgroup form
+// ---------------------------------------------------------------------------
+constexpr int kWideThreads = 256;                  // 4 waves
+constexpr int kWideWaves = kWideThreads / 64;
+constexpr int kWideBatches = 4;                    // 64-slot batches per wave
+constexpr int kWideSlots = kWideThreads * kWideBatches;   // slots per workgroup
+
+__device__ __forceinline__ int expert_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
+
+// Per-wave expert counts of one workgroup's slots into cnt[w * E + e]
+// (cnt zeroed by the caller); ev holds each lane's ids of its 4 batches.
+__device__ __forceinline__ void wide_count(const int (&ev)[kWideBatches], int E, int* cnt) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    const int nbits = expert_bits(E);
+    int* my = cnt + w * E;
+#pragma unroll
+    for (int u = 0; u < kWideBatches; ++u) {
+        const int e = ev[u];
+        const bool valid = e >= 0 && e < E;
+        const uint64_t m = peers(e, valid, nbits);
+        if (valid && (m & lt_mask) == 0) my[e] += __popcll(m);
+    }
+}
+
+__device__ __forceinline__ void wide_load(const int32_t* ids, int R, int (&ev)[kWideBatches]) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int base = blockIdx.x * kWideSlots + w * 64 * kWideBatches;
+#pragma unroll
+    for (int u = 0; u < kWideBatches; ++u) {
+        const int f = base + 64 * u + lane;
+        ev[u] = f < R ? ids[f] : -1;
+    }
+}
+
+// counts[g * E + e] = slots of expert e among workgroup g's slots
+__global__ __launch_bounds__(kWideThreads) void align_count_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                   int32_t* __restrict__ counts) {
+    __shared__ int cnt[kWideWaves * kMaxE];
+    const int tid = threadIdx.x;
+    int ev[kWideBatches];
+    wide_load(ids, R, ev);
+    for (int i = tid; i < kWideWaves * E; i += kWideThreads) cnt[i] = 0;
+    __syncthreads();
+    wide_count(ev, E, cnt);
+    __syncthreads();
+    for (int e = tid; e < E; e += kWideThreads) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kWideWaves; ++w) c += cnt[w * E + e];
+        counts[int64_t(blockIdx.x) * E + e] = c;
+    }
+}
+
+// One workgroup: padded sizes, exclusive scan over experts, the start of
+// every (workgroup, expert) run, padding and tail sentinels, block experts,
+// padded total.  Threads are split as (expert, part): the parts of one
+// expert cover consecutive ranges of workgroups.
+__global__ __launch_bounds__(kThreads) void align_scan_kernel(const int32_t* __restrict__ counts, int ngroups,
+                                                              int R, int E, int B, int cap,
+                                                              int32_t* __restrict__ starts,
+                                                              int32_t* __restrict__ sorted,
+                                                              int32_t* __restrict__ expert_ids,
+                                                              int32_t* __restrict__ ntpp) {
+    __shared__ int part_sum[kThreads];
+    __shared__ int offs[kMaxE + 1];
+    __shared__ int wsum[kWaves];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    int ep = 1;
+    while (ep < E) ep <<= 1;                       // experts rounded up to a power of two
+    const int parts = kThreads / ep;
+    const int e = tid & (ep - 1), part = tid / ep;
+    const int per = (ngroups + parts - 1) / parts;
+    const int q0 = min(ngroups, part * per), q1 = min(ngroups, q0 + per);
+    int local = 0;
+    if (e < E) {
+#pragma unroll 8
+        for (int q = q0; q < q1; ++q) local += counts[int64_t(q) * E + e];
+    }
+    part_sum[tid] = local;
+    __syncthreads();
+
+    int padded = 0, total = 0;
+    if (tid < E) {
+        for (int pp = 0; pp < parts; ++pp) total += part_sum[pp * ep + tid];
+        padded = (total + B - 1) / B * B;
+    }
+    int incl = padded;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+        int s = lane < kWaves ? wsum[lane] : 0;
+        int si = s;
+#pragma unroll
+        for (int d = 1; d < kWaves; d <<= 1) {
+            const int o = __shfl_up(si, d);
+            if (lane >= d) si += o;
+        }
+        if (lane < kWaves) wsum[lane] = si - s;
+    }
+    __syncthreads();
+    if (tid < E) {
+        const int excl = incl - padded + wsum[w];
+        offs[tid] = excl;
+        if (tid == E - 1) offs[E] = excl + padded;
+    }
+    __syncthreads();
+
+    if (e < E) {
+        const int beg = offs[e], end = offs[e + 1];
+        int run = beg;
+        int filled = 0;                            // rows of expert e over all parts
+        for (int pp = 0; pp < parts; ++pp) {
+            const int c = part_sum[pp * ep + e];
+            if (pp < part) run += c;
+            filled += c;
+        }
+#pragma unroll 8
+        for (int q = q0; q < q1; ++q) {
+            const int64_t i = int64_t(q) * E + e;
+            starts[i] = run;
+            run += counts[i];
+        }
+        for (int p = beg + filled + part; p < end; p += parts) sorted[p] = R;               // padding
+        for (int b = beg / B + part; b < end / B; b += parts) expert_ids[b] = e;             // its blocks
+    }
+    const int all = offs[E];
+    if (tid == 0) ntpp[0] = all;
+    for (int p = all + tid; p < cap; p += kThreads) sorted[p] = R;
+    const int nblocks = (cap + B - 1) / B;
+    for (int b = all / B + tid; b < nblocks; b += kThreads) expert_ids[b] = -1;
+}
+
+// Scatter: the workgroup's per-wave counts again (its slots), each wave's
+// start per expert = the workgroup's start + the counts of the waves before
+// it, then the stable scatter.
+__global__ __launch_bounds__(kWideThreads) void align_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                     const int32_t* __restrict__ starts,
+                                                                     int32_t* __restrict__ sorted,
+                                                                     int32_t* __restrict__ inv) {
+    __shared__ int cnt[kWideWaves * kMaxE];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    const int nbits = expert_bits(E);
+    int ev[kWideBatches];
+    wide_load(ids, R, ev);
+    for (int i = tid; i < kWideWaves * E; i += kWideThreads) cnt[i] = 0;
+    __syncthreads();
+    wide_count(ev, E, cnt);
+    __syncthreads();
+    const int32_t* st = starts + int64_t(blockIdx.x) * E;
+    for (int e = tid; e < E; e += kWideThreads) {
+        int run = st[e];
+#pragma unroll
+        for (int ww = 0; ww < kWideWaves; ++ww) {
+            const int c = cnt[ww * E + e];
+            cnt[ww * E + e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    int* my = cnt + w * E;
+    const int base = blockIdx.x * kWideSlots + w * 64 * kWideBatches;
+#pragma unroll
+    for (int u = 0; u < kWideBatches; ++u) {
+        const int f = base + 64 * u + lane;
+        const int e = ev[u];
+        const bool valid = e >= 0 && e < E;
+        const uint64_t m = peers(e, valid, nbits);
+        if (valid) {
+            const int pos = my[e] + __popcll(m & lt_mask);
+            sorted[pos] = f;
+            if (inv) inv[f] = pos;
+        } else if (f < R && inv) {
+            inv[f] = -1;
+        }
+        if (valid && (m & lt_mask) == 0) my[e] += __popcll(m);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_align(const int32_t* ids, int T, int topk, int E, int block_m, int64_t cap,
@@ -173,6 +362,26 @@ hipError_t launch_align(const int32_t* ids, int T, int topk, int E, int block_m,
                         hipStream_t s) {
     hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), 0, s, ids, T * topk, E, block_m,
                        int(cap), sorted_ids, expert_ids, ntpp, inv);
+    return hipGetLastError();
+}
+
+int64_t align_scratch_bytes(int64_t R, int E) {
+    const int64_t groups = (R + kWideSlots - 1) / kWideSlots;
+    return 2 * groups * E * int64_t(sizeof(int32_t));
+}
+
+hipError_t launch_align_wide(const int32_t* ids, int T, int topk, int E, int block_m, int64_t cap,
+                             int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, int32_t* inv,
+                             void* scratch, hipStream_t s) {
+    const int R = T * topk;
+    const int groups = (R + kWideSlots - 1) / kWideSlots;
+    int32_t* counts = static_cast<int32_t*>(scratch);
+    int32_t* starts = counts + int64_t(groups) * E;
+    hipLaunchKernelGGL(align_count_kernel, dim3(groups), dim3(kWideThreads), 0, s, ids, R, E, counts);
+    hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kThreads), 0, s, counts, groups, R, E, block_m, int(cap),
+                       starts, sorted_ids, expert_ids, ntpp);
+    hipLaunchKernelGGL(align_scatter_kernel, dim3(groups), dim3(kWideThreads), 0, s, ids, R, E, starts,
+                       sorted_ids, inv);
     return hipGetLastError();
 }
 

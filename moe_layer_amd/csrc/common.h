@@ -119,6 +119,13 @@ hipError_t launch_align(const int32_t* ids, int T, int topk, int E, int block_m,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, int32_t* inv,
                         hipStream_t s);
 
+// Same output as launch_align, spread over many workgroups; needs
+// align_scratch_bytes(R, E) bytes of scratch (4-byte aligned).
+int64_t align_scratch_bytes(int64_t R, int E);
+hipError_t launch_align_wide(const int32_t* ids, int T, int topk, int E, int block_m, int64_t cap,
+                             int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, int32_t* inv,
+                             void* scratch, hipStream_t s);
+
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
                             hipStream_t s);
 

@@ -3,6 +3,7 @@
 // behaviour are documented in include/moe.h.
 #include "moe.h"
 
+#include <algorithm>
 #include <climits>
 #include <cstddef>
 
@@ -16,6 +17,9 @@ constexpr int kVersionMajor = 1;
 constexpr int kVersionMinor = 0;
 // rows per expert from which the LDS-tiled path beats weight streaming
 constexpr double kLargeMinRowsPerExpert = 96.0;
+// From this many routed slots on, the alignment runs on many workgroups (one
+// workgroup's ALUs bound it above a few thousand slots).
+constexpr int64_t kAlignWideMinSlots = 2048;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -88,7 +92,8 @@ int make_plan(const moe_forward_args* a, Plan* p) {
     p->off_xs = fp8 ? take(int64_t(a->T) * (a->H / MOE_QUANT_GROUP) * 4) : -1;
     p->off_inter = take(rows * a->I * es);
     p->off_inter_scale = fp8 ? take(rows * (a->I / MOE_QUANT_GROUP) * 4) : -1;
-    p->off_y = take(R * a->H * 4);
+    // y also serves as the wide alignment's scratch (used before GEMM2 writes y)
+    p->off_y = take(std::max(R * a->H * 4, align_scratch_bytes(R, a->E)));
     p->total = off;
     return MOE_OK;
 }
@@ -230,11 +235,15 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
 
     auto mark = [&](int i) { return ev ? hip_status(hipEventRecord(ev[i], stream)) : MOE_OK; };
     if ((st = mark(0)) != MOE_OK) return st;
-    if ((st = hip_status(launch_align(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap,
-                                      reinterpret_cast<int32_t*>(ws + p.off_sorted),
-                                      reinterpret_cast<int32_t*>(ws + p.off_eids),
-                                      reinterpret_cast<int32_t*>(ws + p.off_ntpp), nullptr, stream))) != MOE_OK)
-        return st;
+    int32_t* sorted = reinterpret_cast<int32_t*>(ws + p.off_sorted);
+    int32_t* eids = reinterpret_cast<int32_t*>(ws + p.off_eids);
+    int32_t* ntpp = reinterpret_cast<int32_t*>(ws + p.off_ntpp);
+    const hipError_t ae =
+        int64_t(a->T) * a->topk >= kAlignWideMinSlots
+            ? launch_align_wide(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap, sorted, eids, ntpp, nullptr,
+                                ws + p.off_y, stream)
+            : launch_align(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap, sorted, eids, ntpp, nullptr, stream);
+    if ((st = hip_status(ae)) != MOE_OK) return st;
     if ((st = mark(1)) != MOE_OK) return st;
     if (fp8 && (st = hip_status(launch_quant_act(g.x, a->T, a->H, ws + p.off_xq,
                                                  reinterpret_cast<float*>(ws + p.off_xs), stream))) != MOE_OK)

@@ -82,6 +82,35 @@ def test_align_empty_experts_worked_example():
     _check_align(np.array([[3, 1], [1, 3]]), 4, 2)
 
 
+@pytest.mark.parametrize("T,k,E,B", [(16, 8, 128, 16), (255, 8, 64, 32), (256, 8, 64, 32), (1024, 8, 256, 32),
+                                     (1000, 7, 1024, 64), (4096, 8, 128, 256), (8192, 8, 256, 256),
+                                     (3000, 3, 5, 16)])
+def test_forward_alignment_buffers(T, k, E, B):
+    """The alignment moe_forward leaves in its workspace (one workgroup below
+    2048 slots, several above) equals the oracle's, bit for bit."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config("align", T, E, 256, 128, k, "bf16", "given")
+    layer = layer_for(cfg)
+    rng = np.random.default_rng(T * k + E)
+    ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)     # invalid and duplicate ids
+    ids[: T // 3] = rng.integers(0, max(1, E // 8), size=(T // 3, k))  # skewed load
+    tw = np.ones((T, k), np.float32)
+    x = np.zeros((T, 256), np.uint16)
+    out, ws, (xt, ids_t, tw_t) = run_forward(layer, x, ids, tw, block_m=B,
+                                             path=ops.MOE_PATH_LARGE_M if B == 256 else ops.MOE_PATH_SMALL_M)
+    p = ops.moe_plan(ops.forward_args(xt, layer.w13, layer.w2, ids_t, tw_t, None, None, out,
+                                      ops.MOE_PATH_LARGE_M if B == 256 else ops.MOE_PATH_SMALL_M, B))
+    o = O.align(ids, E, B)
+    w = ws.cpu().numpy()
+
+    def buf(off, n):
+        return w[off: off + 4 * n].view(np.int32)
+
+    np.testing.assert_array_equal(buf(p["off_sorted_ids"], p["capacity"]), o["sorted_token_ids"])
+    np.testing.assert_array_equal(buf(p["off_expert_ids"], p["num_blocks"]), o["expert_ids"])
+    assert int(buf(p["off_num_post_padded"], 1)[0]) == o["num_tokens_post_padded"]
+
+
 # ------------------------------------------------------ fp8 activation quant ---
 
 def test_quant_act_bit_exact():
