@@ -150,20 +150,26 @@ struct GemmArgs {
 // Workgroup -> (block, column tile) over the blocks that hold routed rows
 // (the first ntpp / block_m blocks; the rest of the capacity is tail).  The
 // hardware deals workgroups to the 8 XCDs round-robin (workgroup i runs on
-// XCD i % 8).  The active items, ordered tile-major so that the blocks of one
-// expert (same weights) are adjacent, are cut into 8 equal contiguous ranges,
-// one per XCD: every XCD gets the same work, and blocks that share weights run
-// together on one XCD and share its L2.  The grid is sized for the worst case
-// (every capacity block active, 8 | grid); workgroups past their XCD's range
-// exit at once.
+// XCD i % 8).  The active items are cut into 8 equal contiguous ranges, one
+// per XCD, so every XCD gets the same work and neighbouring items share its
+// L2.  Items are ordered tile-major (blocks of one expert, same weights,
+// adjacent) or block-major (the column tiles of one block, same token rows,
+// adjacent).  The grid is sized for the worst case (every capacity block
+// active, 8 | grid); workgroups past their XCD's range exit at once.
+template <bool kBlockMajor = false>
 __device__ __forceinline__ bool map_active_tile(const GemmArgs& g, int ntiles, int& blk, int& tile) {
     const int active = __builtin_amdgcn_readfirstlane(g.ntpp[0]) / g.block_m;
     const int64_t total = int64_t(active) * ntiles;
     const int xcd = blockIdx.x & 7;
     const int64_t item = xcd * total / 8 + (blockIdx.x >> 3);
     if (item >= (xcd + 1) * total / 8) return false;
-    tile = int(item / active);
-    blk = int(item - int64_t(tile) * active);
+    if constexpr (kBlockMajor) {
+        blk = int(item / ntiles);
+        tile = int(item - int64_t(blk) * ntiles);
+    } else {
+        tile = int(item / active);
+        blk = int(item - int64_t(tile) * active);
+    }
     return true;
 }
 

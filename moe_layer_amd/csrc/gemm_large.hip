@@ -41,11 +41,16 @@ constexpr int kTM = 256;           // weight rows per workgroup
 constexpr int kBM = 256;           // tokens per workgroup (= block_m of the alignment)
 constexpr int kKB = 64;            // K per stage (bf16 elements)
 constexpr int kRowBytes = kKB * 2; // 128 bytes per LDS row
-constexpr int kWaves = 8;
+constexpr int kWM = 4;                         // wave groups along the weight rows
+constexpr int kWaves = 2 * kWM;                // x 2 along the tokens
 constexpr int kThreads = 64 * kWaves;
+constexpr int kTW = kTM / kWM;                 // weight rows per wave
+constexpr int kTA = kTW / 32;                  // 32-row A fragments per wave
 constexpr int kTileBytes = 256 * kRowBytes;         // one operand stage: 32 KiB
 constexpr int kStageBytes = 2 * kTileBytes;         // weights + tokens
-constexpr int kLoads = kTileBytes / 16 / kThreads;  // 16-byte loads per thread per operand (4)
+constexpr int kLoads = kTileBytes / 16 / kThreads;  // 16-byte loads per thread per operand
+constexpr int kLoadRows = kThreads / 8;              // tile rows one load step covers (8 chunks a row)
+static_assert(kLoads * kLoadRows == 256, "the loader must cover the 256 tile rows exactly once");
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -54,24 +59,24 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    const int wm = wv & 3, wn = wv >> 2;
+    const int wm = wv % kWM, wn = wv / kWM;
     const int R = g.T * g.topk;
     const int K = GEMM == 1 ? g.H : g.I;
     const int nst = K / kKB;
     const int64_t kbytes = int64_t(K) * 2;
 
-    // ---- global sources: thread tid moves chunk (tid & 7) of rows j*64 + tid/8 --
+    // ---- global sources: thread tid moves chunk (tid & 7) of rows j*kLoadRows + tid/8
     const int chunk = tid & 7;
-    const int row0 = tid >> 3;   // 0..63
+    const int row0 = tid >> 3;   // 0..kLoadRows-1
     const uint8_t* a_src[kLoads];
     const uint8_t* b_src[kLoads];
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
-        const int r = j * 64 + row0;   // tile row 0..255
+        const int r = j * kLoadRows + row0;   // tile row 0..255
         if constexpr (GEMM == 1) {
-            // tile row r = 64w + 32*half + rr: weight-wave w's gate rows, then its up rows
-            const int half = (r >> 5) & 1, rr = r & 31;
-            const int64_t grow = int64_t(e) * 2 * g.I + (half ? g.I : 0) + tile * 128 + (r >> 6) * 32 + rr;
+            // tile row r = kTW*w + (kTW/2)*half + rr: weight-wave w's gate rows, then its up rows
+            const int half = (r / (kTW / 2)) & 1, rr = r % (kTW / 2);
+            const int64_t grow = int64_t(e) * 2 * g.I + (half ? g.I : 0) + tile * 128 + (r / kTW) * (kTW / 2) + rr;
             a_src[j] = static_cast<const uint8_t*>(g.w13) + grow * kbytes + chunk * 16;
             const int f = g.sorted_ids[blk * kBM + r];
             const int tok = f < R ? f / g.topk : 0;   // padding rows read token 0 (never stored as real rows)
@@ -96,14 +101,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
         uint8_t* B = A + kTileBytes;
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            *reinterpret_cast<i32x4*>(A + swz(j * 64 + row0, chunk)) = ra[j];
-            *reinterpret_cast<i32x4*>(B + swz(j * 64 + row0, chunk)) = rb[j];
+            *reinterpret_cast<i32x4*>(A + swz(j * kLoadRows + row0, chunk)) = ra[j];
+            *reinterpret_cast<i32x4*>(B + swz(j * kLoadRows + row0, chunk)) = rb[j];
         }
     };
 
-    f32x16 acc[2][NU > 0 ? NU : 1];
+    f32x16 acc[kTA][NU > 0 ? NU : 1];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < kTA; ++t)
 #pragma unroll
         for (int u = 0; u < (NU > 0 ? NU : 1); ++u)
 #pragma unroll
@@ -111,7 +116,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
 
     const int fr = lane & 31;   // fragment row / column
     const int fk = lane >> 5;   // fragment K half
-    const int arow = wm * 64 + fr;
+    const int arow = wm * kTW + fr;
 
     gload(0);
     lstore(0);
@@ -125,15 +130,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
 #pragma unroll
         for (int s = 0; s < kKB / 16; ++s) {
             const int c = 2 * s + fk;
-            i32x4 af[2], bf[NU > 0 ? NU : 1];
+            i32x4 af[kTA], bf[NU > 0 ? NU : 1];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) af[t] = *reinterpret_cast<const i32x4*>(A + swz(arow + t * 32, c));
+            for (int t = 0; t < kTA; ++t) af[t] = *reinterpret_cast<const i32x4*>(A + swz(arow + t * 32, c));
 #pragma unroll
             for (int u = 0; u < NU; ++u) bf[u] = *reinterpret_cast<const i32x4*>(B + swz((2 * u + wn) * 32 + fr, c));
 #pragma unroll
             for (int u = 0; u < NU; ++u)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < kTA; ++t)
                     acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[t]),
                                                                         __builtin_bit_cast(bf16x8, bf[u]),
                                                                         acc[t][u], 0, 0, 0);
@@ -147,26 +152,31 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
     // ---- epilogues: wave sub-tile u sits at token rows (2u + wn) * 32 ---------
     if constexpr (GEMM == 1) {
         uint16_t* out = static_cast<uint16_t*>(g.inter);
-        const int colw = tile * 128 + wm * 32;
+        constexpr int kG = kTA / 2;   // gate fragments per wave; up fragment t + kG pairs with gate t
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int row = blk * kBM + (2 * u + wn) * 32 + fr;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {   // groups of 4 consecutive columns
-                uint32_t p[2];
+            for (int t = 0; t < kG; ++t) {
+                const int colw = tile * 128 + wm * (kTW / 2) + t * 32;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int i0 = q * 4 + 2 * h;
-                    const float a0 = silu_mul_bf16(round_bf16(acc[0][u][i0]), round_bf16(acc[1][u][i0]));
-                    const float a1 = silu_mul_bf16(round_bf16(acc[0][u][i0 + 1]), round_bf16(acc[1][u][i0 + 1]));
-                    p[h] = uint32_t(f32_to_bf16_rne(a0)) | (uint32_t(f32_to_bf16_rne(a1)) << 16);
+                for (int q = 0; q < 4; ++q) {   // groups of 4 consecutive columns
+                    uint32_t p[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int i0 = q * 4 + 2 * h;
+                        const float a0 = silu_mul_bf16(round_bf16(acc[t][u][i0]), round_bf16(acc[t + kG][u][i0]));
+                        const float a1 =
+                            silu_mul_bf16(round_bf16(acc[t][u][i0 + 1]), round_bf16(acc[t + kG][u][i0 + 1]));
+                        p[h] = uint32_t(f32_to_bf16_rne(a0)) | (uint32_t(f32_to_bf16_rne(a1)) << 16);
+                    }
+                    const int col = colw + q * 8 + fk * 4;
+                    *reinterpret_cast<i32x2*>(out + int64_t(row) * g.I + col) = i32x2{int(p[0]), int(p[1])};
                 }
-                const int col = colw + q * 8 + fk * 4;
-                *reinterpret_cast<i32x2*>(out + int64_t(row) * g.I + col) = i32x2{int(p[0]), int(p[1])};
             }
         }
     } else {
-        const int hw = tile * kTM + wm * 64;
+        const int hw = tile * kTM + wm * kTW;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int f = g.sorted_ids[blk * kBM + (2 * u + wn) * 32 + fr];
@@ -174,7 +184,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
             const float tw = g.topk_weights[f];
             float* yrow = g.y + int64_t(f) * g.H;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < kTA; ++t)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     f32x4 v;
@@ -192,7 +202,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
     __shared__ int s_valid;
 
     int blk, tile;
-    if (!map_active_tile(g, ntiles, blk, tile)) return;
+    // block-major: the 12-24 column tiles of one block share its token rows in
+    // L2, and the blocks of one expert (adjacent) run together and share the
+    // weight tiles (measured: L2 hit rate 17% -> 42% on the prefill layer)
+    if (!map_active_tile<true>(g, ntiles, blk, tile)) return;
     const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
     if (e < 0) return;
 
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
     __syncthreads();
     // live 32-token sub-tiles of this wave: u = wn, wn + 2, ... below the count
     const int live = (s_valid + 31) >> 5;
-    const int wn = (threadIdx.x >> 6) >> 2;
+    const int wn = (threadIdx.x >> 6) / kWM;
     switch ((live - wn + 1) >> 1) {
         case 0: run_tile<GEMM, 0>(g, lds, blk, tile, e); break;
         case 1: run_tile<GEMM, 1>(g, lds, blk, tile, e); break;
