@@ -23,17 +23,32 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
     const int t = int(i / per_row);
     const int h = int(i - int64_t(t) * per_row) * 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < topk; ++j) {
-        const int e = ids[int64_t(t) * topk + j];
-        if (e < 0 || e >= E) continue;
-        const float* row = y + (int64_t(t) * topk + j) * H + h;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(row);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(row + 4);
+    // slots in groups of 8: the ids first, then every y load of the group at
+    // once (an unrouted slot's row is loaded from slot 0's and added as +0.0,
+    // which leaves the sum unchanged bit for bit: it starts at +0.0, so no
+    // partial sum is -0.0)
+    for (int j0 = 0; j0 < topk; j0 += 8) {
+        bool ok[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[q] = __fadd_rn(acc[q], a[q]);
-            acc[4 + q] = __fadd_rn(acc[4 + q], b[q]);
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            const int e = j < topk ? ids[int64_t(t) * topk + j] : -1;
+            ok[u] = e >= 0 && e < E;
         }
+        f32x4 a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float* row = y + (int64_t(t) * topk + (ok[u] ? j0 + u : 0)) * H + h;
+            a[u] = *reinterpret_cast<const f32x4*>(row);
+            b[u] = *reinterpret_cast<const f32x4*>(row + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[q] = __fadd_rn(acc[q], ok[u] ? a[u][q] : 0.0f);
+                acc[4 + q] = __fadd_rn(acc[4 + q], ok[u] ? b[u][q] : 0.0f);
+            }
     }
     i32x4 packed;
 #pragma unroll

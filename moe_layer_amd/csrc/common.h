@@ -174,6 +174,7 @@ __device__ __forceinline__ bool map_active_tile(const GemmArgs& g, int ntiles, i
 }
 
 hipError_t launch_gemm1_small(const GemmArgs& g, bool fp8, hipStream_t s);
+int small_gemm2_cols(int T, int topk, int E, int H, bool fp8, int NT);   // NT = block_m / 16
 hipError_t launch_gemm2_small(const GemmArgs& g, bool fp8, hipStream_t s);
 hipError_t launch_gemm1_large(const GemmArgs& g, bool fp8, hipStream_t s);
 hipError_t launch_gemm2_large(const GemmArgs& g, bool fp8, hipStream_t s);

@@ -411,17 +411,26 @@ hipError_t gemm2_dispatch(const GemmArgs& g, hipStream_t s) {
         // K = I is short: 64 output rows per wave keep more bytes in flight
         // (32 for 64-token blocks, registers; 32 when H % 256 != 0)
         if constexpr (NT <= 2) {
-            if (g.H % 256 == 0) return gemm2_fp8<NT, 4>(g, s);
+            if (small_gemm2_cols(g.T, g.topk, g.E, g.H, true, NT) == 256) return gemm2_fp8<NT, 4>(g, s);
         }
         return gemm2_fp8<NT, 2>(g, s);
     } else {
-        // 128 output columns per workgroup, or 64 when H is not a multiple of 128
-        if (g.H % 128 == 0) return gemm2_bf16<NT, 2>(g, s);
+        // 128 output columns per workgroup, or 64 when H is not a multiple of
+        // 128 (narrower tiles for one or two decode tokens measured slower)
+        if (small_gemm2_cols(g.T, g.topk, g.E, g.H, false, NT) == 128) return gemm2_bf16<NT, 2>(g, s);
         return gemm2_bf16<NT, 1>(g, s);
     }
 }
 
 }  // namespace
+
+// GEMM2 output rows of H per workgroup on the weight-streaming path (the
+// dispatch above follows the same rule)
+int small_gemm2_cols(int T, int topk, int E, int H, bool fp8, int NT) {
+    (void)T, (void)topk, (void)E;
+    if (fp8) return (NT <= 2 && H % 256 == 0) ? 256 : 128;
+    return H % 128 == 0 ? 128 : 64;
+}
 
 hipError_t launch_gemm1_small(const GemmArgs& g, bool fp8, hipStream_t s) {
     switch (g.block_m) {

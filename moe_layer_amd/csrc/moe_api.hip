@@ -78,7 +78,7 @@ int make_plan(const moe_forward_args* a, Plan* p) {
         p->gemm2_cols = 256;
     } else {
         p->gemm1_cols = fp8 ? 256 : 128;   // gate + up rows per workgroup
-        p->gemm2_cols = (fp8 || a->H % 128 == 0) ? 128 : 64;
+        p->gemm2_cols = small_gemm2_cols(a->T, a->topk, a->E, a->H, fp8, bm / 16);
     }
 
     const int64_t rows = int64_t(p->num_blocks) * bm;   // every row a block can touch
