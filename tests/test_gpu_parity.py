@@ -254,6 +254,28 @@ def test_forward_ragged_shapes(wdtype):
         assert excess <= TAU[wdtype]
 
 
+@pytest.mark.parametrize("H,I", [(8448, 384), (8320, 256)])
+def test_forward_fp8_long_k(H, I):
+    """fp8 with more than 64 K-blocks of 128 (the activation-scale table is
+    staged in two chunks), an odd K-block count in GEMM2, and H not a
+    multiple of 256 (the narrower GEMM2 tile)."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config("fp8_longk", 20, 6, H, I, 2, "fp8", "given")
+    wl = Workload(cfg)
+    rng = np.random.default_rng(H + I)
+    ids = np.stack([rng.permutation(6)[:2] for _ in range(20)]).astype(np.int32)
+    tw = rng.random((20, 2)).astype(np.float32)
+    layer = layer_for(cfg)
+    layer.ensure(range(6))
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(20))
+    for bm in (16, 32, 64):
+        out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=bm)
+        gpu = out.to(torch.float64).cpu().numpy()
+        excess, raw, _ = compare_output(gpu, o)
+        log(f"fp8 H={H} I={I} bm={bm}: excess/RMS={excess:.3e} raw={raw:.3e}")
+        assert excess <= TAU["fp8"]
+
+
 # ------------------------------------------------------ self-consistency ---
 
 def _layer_inputs(cfg):
