@@ -4,8 +4,9 @@
 One step = one pass of the whole layer over one batch of synthetic tokens,
 inputs resident in HBM: moe_route (router softmax + top-k on fp32 logits) and
 moe_forward (alignment, [fp8 activation quant], GEMM1 + SiLU-mul epilogue,
-GEMM2 with the router weight, top-k combine).  The fp8 workload is handed its
-routing, as the pages' block-fp8 test is, so its step is moe_forward alone.
+GEMM2 with the router weight, top-k combine).  The fp8 and mxfp8 workloads are
+handed their routing, as the pages' block-fp8 test is, so their step is
+moe_forward alone.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 
@@ -30,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused-MoE layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s % of peak"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "fp8", "skew"])
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "fp8", "mxfp8", "skew"])
     ap.add_argument("--tokens", type=int, default=None, help="use the first T tokens of the workload")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--path", type=int, default=0)
@@ -56,7 +57,8 @@ def parse():
 
 # sources each dominant kernel is built from (its HBM traffic counters are
 # valid only while these are unchanged)
-KERNEL_SOURCES = {"small": ("gemm_small.hip", "common.h"), "large": ("gemm_large.hip", "common.h")}
+KERNEL_SOURCES = {"small": ("gemm_small.hip", "common.h"), "large": ("gemm_large.hip", "common.h"),
+                  "mx": ("gemm_mx.hip", "common.h")}
 
 
 def kernel_source_digest(path: str) -> str:
@@ -96,7 +98,8 @@ def main():
     if args.tokens:
         cfg = cfg.with_tokens(args.tokens)
     wl = Workload(cfg)
-    fp8 = cfg.wdtype == "fp8"
+    fp8 = cfg.wdtype in ("fp8", "mxfp8")
+    mx = cfg.wdtype == "mxfp8"
     T, E, H, I, k = cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk
     log(f"workload {cfg.name} T={T} E={E} H={H} I={I} k={k} {cfg.wdtype}")
 
@@ -114,7 +117,12 @@ def main():
     active = np.unique(ids_host[(ids_host >= 0) & (ids_host < E)])
     log(f"{len(active)} active experts; drawing and uploading their weights")
 
-    if fp8:
+    if mx:
+        w13 = torch.zeros((E, 2 * I, H), dtype=torch.uint8, device=d)
+        w2 = torch.zeros((E, H, I), dtype=torch.uint8, device=d)
+        s13 = torch.full((E, 2 * I, H // 32), 127, dtype=torch.uint8, device=d)
+        s2 = torch.full((E, H, I // 32), 127, dtype=torch.uint8, device=d)
+    elif fp8:
         w13 = torch.zeros((E, 2 * I, H), dtype=torch.uint8, device=d)
         w2 = torch.zeros((E, H, I), dtype=torch.uint8, device=d)
         s13 = torch.ones((E, 2 * I // 128, H // 128), dtype=torch.float32, device=d)
@@ -200,15 +208,19 @@ def main():
     bw = 1 if fp8 else 2
     na = len(active)
     R = T * k
-    w13_bytes = na * 2 * I * H * bw + (na * (2 * I // 128) * (H // 128) * 4 if fp8 else 0)
-    w2_bytes = na * H * I * bw + (na * (H // 128) * (I // 128) * 4 if fp8 else 0)
+    # weight scales: fp32 per 128x128 block (fp8) or one E8M0 byte per 32 (mxfp8)
+    sc = (lambda n, kk: n * kk // 32) if mx else (lambda n, kk: (n // 128) * (kk // 128) * 4) if fp8 \
+        else (lambda n, kk: 0)
+    w13_bytes = na * (2 * I * H * bw + sc(2 * I, H))
+    w2_bytes = na * (H * I * bw + sc(H, I))
     x_bytes = T * H * 2
     out_bytes = T * H * 2
     route_bytes = T * k * 8 + (T * E * 4 if logits is not None else 0)
     layer_bytes = w13_bytes + w2_bytes + x_bytes + out_bytes + route_bytes
     layer_flops = 6.0 * R * H * I
     # GEMM1: weights of the active experts, activations in, intermediate out
-    g1_bytes = w13_bytes + (T * H * (1 + 4 / 128) if fp8 else x_bytes) + R * I * (1 + 4 / 128 if fp8 else 2)
+    act_scale = 1 / 32 if mx else 4 / 128   # activation scale bytes per element (fp8 paths)
+    g1_bytes = w13_bytes + (T * H * (1 + act_scale) if fp8 else x_bytes) + R * I * (1 + act_scale if fp8 else 2)
     g1_flops = 4.0 * R * H * I
     g1_ms = stage_ms[2]
     # The dominant kernel's roofline: its lower bound is the larger of
@@ -225,9 +237,10 @@ def main():
         roof = {"bound": "mfma", "achieved": round(g1_tfs, 2), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(g1_tfs / peak_tf, 4)}
     large = plan["path"] == 2
-    digest = kernel_source_digest("large" if large else "small")
+    digest = kernel_source_digest("large" if large else "mx" if mx else "small")
     roof["traffic"] = read_traffic(cfg.name if not args.tokens else f"{cfg.name}@{T}", digest)
     roof["kernel"] = ("gemm_large_kernel<1> (LDS-tiled GEMM1 + SiLU-mul epilogue)" if large
+                      else "gemm1_mx_kernel (weight-streaming MXFP8 GEMM1 + SiLU-mul-quant epilogue)" if mx
                       else "gemm1_small_kernel (weight-streaming GEMM1 + SiLU-mul epilogue)")
     roof["kernel_ms"] = round(float(g1_ms), 5)
     roof["algorithmic_bytes"] = int(g1_bytes)
@@ -272,7 +285,8 @@ def cpu_baseline(cfg, wl, ids, tw32, host_w, n, routed_from_logits):
     except Exception:
         cores = os.cpu_count() or 1
     E, H, I = cfg.E, cfg.H, cfg.I
-    fp8 = cfg.wdtype == "fp8"
+    fp8 = cfg.wdtype in ("fp8", "mxfp8")
+    mx = cfg.wdtype == "mxfp8"
     x64 = wl.x_exact()[:n]
     # only the sample's experts, renumbered 0..m-1 (ids are remapped the same way)
     experts = sorted(host_w)
@@ -282,7 +296,9 @@ def cpu_baseline(cfg, wl, ids, tw32, host_w, n, routed_from_logits):
     w2 = np.empty((len(experts), H, I))
     for i, e in enumerate(experts):
         c13, s13, c2, s2 = host_w[e]
-        if fp8:
+        if mx:
+            w13[i], w2[i] = O.dequant_mx(c13, s13), O.dequant_mx(c2, s2)
+        elif fp8:
             w13[i], w2[i] = O.dequant_block(c13, s13), O.dequant_block(c2, s2)
         else:
             w13[i], w2[i] = O.bf16_bits_to_f64(c13), O.bf16_bits_to_f64(c2)
@@ -294,7 +310,7 @@ def cpu_baseline(cfg, wl, ids, tw32, host_w, n, routed_from_logits):
             ids_o, tw_o = O.route(lg, cfg.topk)
         else:
             ids_o, tw_o = ids[:n], tw32[:n].astype(np.float64)
-        O.forward(x64, w13, w2, remap[ids_o], tw_o, fp8=fp8)
+        O.forward(x64, w13, w2, remap[ids_o], tw_o, fp8=fp8, group=32 if mx else 128)
         t_total += time.perf_counter() - t0
         reps += 1
     t = t_total / reps

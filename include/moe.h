@@ -52,6 +52,8 @@ extern "C" {
 /* weight element types */
 #define MOE_WDTYPE_BF16      0   /* w13/w2 are bf16 */
 #define MOE_WDTYPE_FP8_E4M3  1   /* w13/w2 are E4M3FN with 128x128 fp32 block scales */
+#define MOE_WDTYPE_MXFP8     2   /* w13/w2 are E4M3FN with one E8M0 scale per row and
+                                    32 consecutive K elements (MXFP8) */
 
 /* GEMM tile path (moe_forward_args.path) */
 #define MOE_PATH_AUTO        0   /* the planner decides from rows per expert */
@@ -62,6 +64,7 @@ extern "C" {
 #define MOE_MAX_EXPERTS      1024
 #define MOE_MAX_TOPK         64
 #define MOE_QUANT_GROUP      128  /* fp8 activation group and weight block edge */
+#define MOE_MX_BLOCK         32   /* MXFP8 block: elements sharing one E8M0 scale */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 MOE_API const char* moe_status_string(int status);
@@ -145,6 +148,21 @@ MOE_API int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t 
 MOE_API int moe_quant_act(const void* x, int32_t rows, int32_t cols, uint8_t* codes,
                           float* scales, hipStream_t stream);
 
+/*
+ * moe_quant_act_mx — the same quantisation on 1x32 groups, scales stored as
+ * E8M0 bytes (value 2^(byte - 127)): the activation side of the MXFP8 layer
+ * (P3, the quantisation section of "Hosting Qwen on Blackwell": MXFP8, the
+ * successor of block scaling; the scale rule is P2 section 1.2's, whose
+ * power-of-two scales E8M0 holds exactly).
+ *
+ *   x       device, bf16 [rows, cols]
+ *   codes   device, E4M3FN [rows, cols]            (output)
+ *   scales  device, E8M0 bytes [rows, cols / 32]   (output)
+ * Requires cols % 32 == 0; codes 8-byte and scales 4-byte aligned.
+ */
+MOE_API int moe_quant_act_mx(const void* x, int32_t rows, int32_t cols, uint8_t* codes,
+                             uint8_t* scales, hipStream_t stream);
+
 /* Arguments of moe_forward (the pages' `apply(x, w1, w2, topk_weights,
  * topk_ids, activation=SiLU, expert_map=None,
  * apply_router_weight_on_input=False)`, P2 section 1.1). */
@@ -157,9 +175,11 @@ typedef struct moe_forward_args {
     int32_t wdtype;       /* MOE_WDTYPE_* */
     const void* x;        /* device bf16 [T, H] */
     const void* w13;      /* device [E, 2I, H]: rows [0, I) gate, [I, 2I) up */
-    const float* w13_scale; /* device fp32 [E, 2I/128, H/128] (fp8 only, else NULL) */
+    const void* w13_scale;  /* FP8_E4M3: device fp32 [E, 2I/128, H/128];
+                               MXFP8: device E8M0 bytes [E, 2I, H/32]; else NULL */
     const void* w2;       /* device [E, H, I] */
-    const float* w2_scale;  /* device fp32 [E, H/128, I/128] (fp8 only, else NULL) */
+    const void* w2_scale;   /* FP8_E4M3: device fp32 [E, H/128, I/128];
+                               MXFP8: device E8M0 bytes [E, H, I/32]; else NULL */
     const int32_t* topk_ids;   /* device int32 [T, topk] */
     const float* topk_weights; /* device fp32 [T, topk] */
     void* out;            /* device bf16 [T, H] (output) */
@@ -201,16 +221,21 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  *   router weight applied in fp32 after the GEMM (P2 section 1.1) ->
  *   out_t = bf16(sum_j y_{t,j}) summed in fp32 in slot order j = 0..topk-1
  *   (the expert aggregation of P1, "Backend-Wechsel").
- * fp8 weights arrive pre-quantised with their fp32 block scales; the library
+ * MXFP8: the same with x and the intermediate quantised per row and
+ * 32-group, scales as E8M0 bytes, and every 32-element block of a product
+ * scaled by its two E8M0 scales inside the matrix-core instruction.
+ * fp8 and MXFP8 weights arrive pre-quantised with their scales; the library
  * never quantises weights.
  *
  *   workspace  device buffer of at least moe_forward_workspace(a) bytes,
  *              256-byte aligned; its contents on entry do not matter and on
  *              exit hold the intermediates (layout in moe_plan_info).
- * Limits: bf16 requires H % 64 == 0 and I % 64 == 0; fp8 requires
+ * Limits: bf16 requires H % 64 == 0 and I % 64 == 0; fp8 and MXFP8 require
  * H % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED).  The large-M
  * path needs bf16 weights, H % 256 == 0 and I % 128 == 0; AUTO takes it from
  * 96 routed rows per expert on, forcing it elsewhere is MOE_ERR_UNSUPPORTED.
+ * The workspace's activation scales (off_xs, off_inter_scale) are fp32 for
+ * FP8_E4M3 and E8M0 bytes for MXFP8.
  */
 MOE_API int moe_forward(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
                         hipStream_t stream);

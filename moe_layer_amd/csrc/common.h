@@ -128,22 +128,24 @@ hipError_t launch_align_wide(const int32_t* ids, int T, int topk, int E, int blo
 
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
                             hipStream_t s);
+hipError_t launch_quant_act_mx(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
+                               hipStream_t s);
 
 struct GemmArgs {
     int T, E, H, I, topk, block_m, num_blocks;
     const uint16_t* x;          // bf16 [T,H]
     const uint8_t* xq;          // fp8 [T,H]
-    const float* xs;            // fp32 [T,H/128]
+    const float* xs;            // fp32 [T,H/128] (fp8) or E8M0 bytes [T,H/32] (MXFP8)
     const void* w13;
-    const float* w13_scale;
+    const void* w13_scale;      // fp32 [E,2I/128,H/128] (fp8) or E8M0 [E,2I,H/32] (MXFP8)
     const void* w2;
-    const float* w2_scale;
+    const void* w2_scale;       // fp32 [E,H/128,I/128] (fp8) or E8M0 [E,H,I/32] (MXFP8)
     const float* topk_weights;  // [T*topk]
     const int32_t* sorted_ids;  // [cap]
     const int32_t* expert_ids;  // [num_blocks]
     const int32_t* ntpp;        // [1]
     void* inter;                // bf16 or fp8 [cap, I]
-    float* inter_scale;         // fp32 [cap, I/128]
+    float* inter_scale;         // fp32 [cap, I/128] (fp8) or E8M0 bytes [cap, I/32] (MXFP8)
     float* y;                   // fp32 [T*topk, H]
 };
 
@@ -176,6 +178,8 @@ __device__ __forceinline__ bool map_active_tile(const GemmArgs& g, int ntiles, i
 hipError_t launch_gemm1_small(const GemmArgs& g, bool fp8, hipStream_t s);
 int small_gemm2_cols(int T, int topk, int E, int H, bool fp8, int NT);   // NT = block_m / 16
 hipError_t launch_gemm2_small(const GemmArgs& g, bool fp8, hipStream_t s);
+hipError_t launch_gemm1_mx(const GemmArgs& g, hipStream_t s);   // MXFP8, block_m 16/32/64
+hipError_t launch_gemm2_mx(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm1_large(const GemmArgs& g, bool fp8, hipStream_t s);
 hipError_t launch_gemm2_large(const GemmArgs& g, bool fp8, hipStream_t s);
 bool gemm_large_supported(int H, int I, bool fp8);   // shapes the LDS-tiled path handles

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(NW * 64) void gemm1_small_kernel(GemmArgs g, int nt
     for (int m = 0; m < MT; ++m) {
         const int row = (m < WT ? i0 + m * 16 : I + i0 + (m - WT) * 16);
         ap[m] = w13 + (int64_t(e) * 2 * I + row + lr) * H * O::kElem + lk * O::kLaneOff;
-        asp[m] = FP8 ? g.w13_scale + (int64_t(e) * (2 * I / kGroup) + row / kGroup) * kb_count : nullptr;
+        asp[m] = FP8 ? static_cast<const float*>(g.w13_scale) + (int64_t(e) * (2 * I / kGroup) + row / kGroup) * kb_count
+                     : nullptr;
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -328,7 +329,8 @@ __global__ __launch_bounds__(NW * 64) void gemm2_small_kernel(GemmArgs g, int nt
     for (int m = 0; m < MT; ++m) {
         const int row = h0 + m * 16;
         ap[m] = w2 + (int64_t(e) * H + row + lr) * I * O::kElem + lk * O::kLaneOff;
-        asp[m] = FP8 ? g.w2_scale + (int64_t(e) * (H / kGroup) + row / kGroup) * kb_count : nullptr;
+        asp[m] = FP8 ? static_cast<const float*>(g.w2_scale) + (int64_t(e) * (H / kGroup) + row / kGroup) * kb_count
+                     : nullptr;
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {

@@ -14,7 +14,7 @@ using namespace moe;
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 0;
+constexpr int kVersionMinor = 1;   // 1.1: MXFP8 weights
 // rows per expert from which the LDS-tiled path beats weight streaming
 constexpr double kLargeMinRowsPerExpert = 96.0;
 // From this many routed slots on, the alignment runs on many workgroups (one
@@ -39,11 +39,12 @@ int validate_forward_scalars(const moe_forward_args* a) {
     if (a->T < 0 || a->E < 1 || a->E > MOE_MAX_EXPERTS || a->topk < 1 || a->topk > MOE_MAX_TOPK ||
         a->H <= 0 || a->I <= 0)
         return MOE_ERR_INVALID_ARG;
-    if (a->wdtype != MOE_WDTYPE_BF16 && a->wdtype != MOE_WDTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+    if (a->wdtype != MOE_WDTYPE_BF16 && a->wdtype != MOE_WDTYPE_FP8_E4M3 && a->wdtype != MOE_WDTYPE_MXFP8)
+        return MOE_ERR_INVALID_ARG;
     if (a->path < MOE_PATH_AUTO || a->path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
     if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 256)
         return MOE_ERR_UNSUPPORTED;
-    const int q = a->wdtype == MOE_WDTYPE_FP8_E4M3 ? MOE_QUANT_GROUP : 64;
+    const int q = a->wdtype == MOE_WDTYPE_BF16 ? 64 : MOE_QUANT_GROUP;
     if (a->H % q != 0 || a->I % q != 0) return MOE_ERR_UNSUPPORTED;
     if (int64_t(a->T) * a->topk > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -53,7 +54,8 @@ int make_plan(const moe_forward_args* a, Plan* p) {
     int st = validate_forward_scalars(a);
     if (st != MOE_OK) return st;
     const int64_t R = int64_t(a->T) * a->topk;
-    const bool fp8 = a->wdtype == MOE_WDTYPE_FP8_E4M3;
+    const bool fp8 = a->wdtype != MOE_WDTYPE_BF16;          // block-scaled fp8 or MXFP8
+    const bool mx = a->wdtype == MOE_WDTYPE_MXFP8;
     const double rows_per_expert = double(R) / a->E;
     const bool large_ok = gemm_large_supported(a->H, a->I, fp8);
     int path = a->path;
@@ -78,7 +80,7 @@ int make_plan(const moe_forward_args* a, Plan* p) {
         p->gemm2_cols = 256;
     } else {
         p->gemm1_cols = fp8 ? 256 : 128;   // gate + up rows per workgroup
-        p->gemm2_cols = small_gemm2_cols(a->T, a->topk, a->E, a->H, fp8, bm / 16);
+        p->gemm2_cols = small_gemm2_cols(a->T, a->topk, a->E, a->H, fp8, bm / 16);   // same tiles for MXFP8
     }
 
     const int64_t rows = int64_t(p->num_blocks) * bm;   // every row a block can touch
@@ -89,9 +91,11 @@ int make_plan(const moe_forward_args* a, Plan* p) {
     p->off_eids = take(int64_t(p->num_blocks) * 4);
     p->off_ntpp = take(4);
     p->off_xq = fp8 ? take(int64_t(a->T) * a->H) : -1;
-    p->off_xs = fp8 ? take(int64_t(a->T) * (a->H / MOE_QUANT_GROUP) * 4) : -1;
+    p->off_xs = mx ? take(int64_t(a->T) * (a->H / MOE_MX_BLOCK)) : fp8 ? take(int64_t(a->T) * (a->H / MOE_QUANT_GROUP) * 4) : -1;
     p->off_inter = take(rows * a->I * es);
-    p->off_inter_scale = fp8 ? take(rows * (a->I / MOE_QUANT_GROUP) * 4) : -1;
+    p->off_inter_scale = mx    ? take(rows * (a->I / MOE_MX_BLOCK))
+                         : fp8 ? take(rows * (a->I / MOE_QUANT_GROUP) * 4)
+                               : -1;
     // y also serves as the wide alignment's scratch (used before GEMM2 writes y)
     p->off_y = take(std::max(R * a->H * 4, align_scratch_bytes(R, a->E)));
     p->total = off;
@@ -160,6 +164,16 @@ MOE_API int moe_quant_act(const void* x, int32_t rows, int32_t cols, uint8_t* co
     return hip_status(launch_quant_act(static_cast<const uint16_t*>(x), rows, cols, codes, scales, stream));
 }
 
+MOE_API int moe_quant_act_mx(const void* x, int32_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                             hipStream_t stream) {
+    if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+    if (cols % MOE_MX_BLOCK != 0) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_quant_act_mx(static_cast<const uint16_t*>(x), rows, cols, codes, scales, stream));
+}
+
 MOE_API int moe_plan(const moe_forward_args* a, moe_plan_info* out) {
     if (!out) return MOE_ERR_INVALID_ARG;
     Plan p;
@@ -200,7 +214,8 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
     int st = make_plan(a, &p);
     if (st != MOE_OK) return st;
     if (a->T == 0) return MOE_OK;
-    const bool fp8 = a->wdtype == MOE_WDTYPE_FP8_E4M3;
+    const bool fp8 = a->wdtype != MOE_WDTYPE_BF16;          // block-scaled fp8 or MXFP8
+    const bool mx = a->wdtype == MOE_WDTYPE_MXFP8;
     if (!a->x || !a->w13 || !a->w2 || !a->topk_ids || !a->topk_weights || !a->out ||
         !aligned(a->x, 16) || !aligned(a->w13, 16) || !aligned(a->w2, 16) || !aligned(a->out, 16) ||
         !aligned(a->topk_ids, 4) || !aligned(a->topk_weights, 4))
@@ -245,16 +260,23 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
             : launch_align(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap, sorted, eids, ntpp, nullptr, stream);
     if ((st = hip_status(ae)) != MOE_OK) return st;
     if ((st = mark(1)) != MOE_OK) return st;
-    if (fp8 && (st = hip_status(launch_quant_act(g.x, a->T, a->H, ws + p.off_xq,
-                                                 reinterpret_cast<float*>(ws + p.off_xs), stream))) != MOE_OK)
-        return st;
+    if (fp8) {
+        const hipError_t qe = mx ? launch_quant_act_mx(g.x, a->T, a->H, ws + p.off_xq, ws + p.off_xs, stream)
+                                 : launch_quant_act(g.x, a->T, a->H, ws + p.off_xq,
+                                                    reinterpret_cast<float*>(ws + p.off_xs), stream);
+        if ((st = hip_status(qe)) != MOE_OK) return st;
+    }
     if ((st = mark(2)) != MOE_OK) return st;
     const bool large = p.path == MOE_PATH_LARGE_M;
-    if ((st = hip_status(large ? launch_gemm1_large(g, fp8, stream) : launch_gemm1_small(g, fp8, stream))) != MOE_OK)
-        return st;
+    const hipError_t g1 = large ? launch_gemm1_large(g, fp8, stream)
+                          : mx  ? launch_gemm1_mx(g, stream)
+                                : launch_gemm1_small(g, fp8, stream);
+    if ((st = hip_status(g1)) != MOE_OK) return st;
     if ((st = mark(3)) != MOE_OK) return st;
-    if ((st = hip_status(large ? launch_gemm2_large(g, fp8, stream) : launch_gemm2_small(g, fp8, stream))) != MOE_OK)
-        return st;
+    const hipError_t g2 = large ? launch_gemm2_large(g, fp8, stream)
+                          : mx  ? launch_gemm2_mx(g, stream)
+                                : launch_gemm2_small(g, fp8, stream);
+    if ((st = hip_status(g2)) != MOE_OK) return st;
     if ((st = mark(4)) != MOE_OK) return st;
     if ((st = hip_status(launch_combine(g.y, a->topk_ids, a->T, a->topk, a->E, a->H,
                                         static_cast<uint16_t*>(a->out), stream))) != MOE_OK)

@@ -17,13 +17,14 @@ _LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(os.path.dirname(os.
 _lib = None
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_WDTYPE_BF16, MOE_WDTYPE_FP8_E4M3 = 0, 1
+MOE_WDTYPE_BF16, MOE_WDTYPE_FP8_E4M3, MOE_WDTYPE_MXFP8 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_SMALL_M, MOE_PATH_LARGE_M = 0, 1, 2
-MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_QUANT_GROUP = 1024, 64, 128
+MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_QUANT_GROUP, MOE_MX_BLOCK = 1024, 64, 128, 32
 
 # every entry point include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_version", "moe_route", "moe_align_capacity", "moe_align",
-           "moe_quant_act", "moe_plan", "moe_forward_workspace", "moe_forward", "moe_forward_profiled")
+           "moe_quant_act", "moe_quant_act_mx", "moe_plan", "moe_forward_workspace", "moe_forward",
+           "moe_forward_profiled")
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("align", "quant_act", "gemm1", "gemm2", "combine")
 
@@ -71,6 +72,8 @@ def lib() -> C.CDLL:
         L.moe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.moe_quant_act.restype = C.c_int
         L.moe_quant_act.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_quant_act_mx.restype = C.c_int
+        L.moe_quant_act_mx.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_plan.restype = C.c_int
         L.moe_plan.argtypes = [C.POINTER(ForwardArgs), C.POINTER(PlanInfo)]
         L.moe_forward_workspace.restype = i64
@@ -152,6 +155,18 @@ def moe_quant_act(x: torch.Tensor):
     return codes, scales
 
 
+def moe_quant_act_mx(x: torch.Tensor):
+    """Per-row, per-32-column MXFP8 quantisation of bf16 x; returns (codes uint8,
+    E8M0 scale bytes uint8)."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.dim() == 2
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, max(cols // MOE_MX_BLOCK, 1)), dtype=torch.uint8, device=x.device)
+    _check("moe_quant_act_mx", lib().moe_quant_act_mx(_ptr(x), rows, cols, _ptr(codes), _ptr(scales),
+                                                      _stream(x.device)))
+    return codes, scales
+
+
 def _u8(t):
     if t is None:
         return None
@@ -167,7 +182,10 @@ def forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=No
         E, twoI, _ = w13.shape
         topk = topk_ids.shape[1]
         fp8 = w13.dtype in (torch.uint8, torch.float8_e4m3fn)
-        shape = (T, E, H, twoI // 2, topk, MOE_WDTYPE_FP8_E4M3 if fp8 else MOE_WDTYPE_BF16)
+        # fp8 weights with fp32 block scales, or with E8M0 byte scales (MXFP8)
+        mx = fp8 and w13_scale is not None and w13_scale.dtype == torch.uint8
+        shape = (T, E, H, twoI // 2, topk,
+                 MOE_WDTYPE_MXFP8 if mx else MOE_WDTYPE_FP8_E4M3 if fp8 else MOE_WDTYPE_BF16)
     T, E, H, I, topk, wdtype = shape
     a = ForwardArgs()
     a.T, a.E, a.H, a.I, a.topk, a.wdtype = T, E, H, I, topk, wdtype
@@ -193,8 +211,9 @@ def moe_forward_workspace(args: ForwardArgs) -> int:
 
 def moe_forward(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=None, out=None,
                 workspace=None, path=MOE_PATH_AUTO, block_m=0):
-    """The fused MoE layer: bf16 x [T,H], w13 [E,2I,H], w2 [E,H,I] (bf16, or
-    e4m3 with fp32 128x128 block scales), int32 ids [T,k], fp32 weights [T,k].
+    """The fused MoE layer: bf16 x [T,H], w13 [E,2I,H], w2 [E,H,I] (bf16; or
+    e4m3 with fp32 128x128 block scales; or e4m3 with E8M0 uint8 scales per row
+    and 32 K elements, MXFP8), int32 ids [T,k], fp32 weights [T,k].
     Returns (out bf16 [T,H], workspace)."""
     T, H = x.shape
     if out is None:

@@ -14,6 +14,7 @@ E=256, H=4096, I=256, topk=8, 128x128 weight blocks; softmax router weights):
   decode   T=16   E=128 H=4096 I=1536 k=8  bf16
   prefill  T=4096 E=128 H=4096 I=1536 k=8  bf16
   fp8      T=1024 E=256 H=4096 I=256  k=8  e4m3 weights, 128x128 fp32 scales
+  mxfp8    T=1024 E=256 H=4096 I=256  k=8  e4m3 weights, E8M0 scale per row and 32 K
   skew     T=8192 E=256 H=7168 I=2048 k=8  bf16, Zipf-biased router logits
 
 Distributions: x ~ N(0, 0.1^2); router matrix W_r ~ N(0, 0.02^2); w13 rows
@@ -44,7 +45,7 @@ class Config:
     H: int
     I: int
     topk: int
-    wdtype: str            # "bf16" or "fp8"
+    wdtype: str            # "bf16", "fp8" (128x128 block scales) or "mxfp8"
     routing: str           # "logits" (route from router logits) or "given"
     skew: bool = False
     seed: int = 0
@@ -58,6 +59,7 @@ CONFIGS = {
     "decode": Config("decode", 16, 128, 4096, 1536, 8, "bf16", "logits"),
     "prefill": Config("prefill", 4096, 128, 4096, 1536, 8, "bf16", "logits"),
     "fp8": Config("fp8", 1024, 256, 4096, 256, 8, "fp8", "given"),
+    "mxfp8": Config("mxfp8", 1024, 256, 4096, 256, 8, "mxfp8", "given"),
     "skew": Config("skew", 8192, 256, 7168, 2048, 8, "bf16", "logits", skew=True),
 }
 
@@ -106,6 +108,25 @@ def quantize_weight_block_fp8(w: np.ndarray, block: int = 128):
     q = np.clip(q, -448.0, 448.0).reshape(N, K)
     codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     return codes, scale
+
+
+def quantize_weight_mx(w: np.ndarray, block: int = 32):
+    """Static MXFP8 conversion done by the caller, as the OCP microscaling
+    format defines it: per row and 32-element block along K the shared
+    exponent is floor(log2 amax) - 8 (8 = the largest e4m3 exponent), stored
+    as an E8M0 byte (exponent + 127), and the elements are w / 2^exponent
+    clamped to +-448 and cast with torch's CPU cast (E4M3FN, nearest even).
+    Returns (codes uint8 [N, K], scales uint8 [N, K/32])."""
+    import torch
+    N, K = w.shape
+    wb = np.ascontiguousarray(w, dtype=np.float32).reshape(N, K // block, block)
+    amax = np.abs(wb).max(axis=2).astype(np.float64)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))          # amax = m 2^e, m in [0.5, 1)
+    x = np.where(amax > 0, e - 1 - 8, -127).clip(-127, 127)
+    q = (wb.astype(np.float64) / np.ldexp(1.0, x)[:, :, None]).astype(np.float32)
+    q = np.clip(q, -448.0, 448.0).reshape(N, K)
+    codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, (x + 127).astype(np.uint8)
 
 
 class Workload:
@@ -195,10 +216,15 @@ class Workload:
     def expert_weights(self, e: int):
         """Layer-format weights of expert e.
         bf16: (w13 bits uint16 [2I,H], None, w2 bits uint16 [H,I], None)
-        fp8 : (w13 codes, w13 scales [2I/128,H/128], w2 codes, w2 scales)"""
+        fp8 : (w13 codes, w13 scales [2I/128,H/128], w2 codes, w2 scales)
+        mxfp8: (w13 codes, w13 E8M0 [2I,H/32], w2 codes, w2 E8M0 [H,I/32])"""
         w13, w2 = self.w13_f32(e), self.w2_f32(e)
         if self.cfg.wdtype == "bf16":
             return to_bf16_bits(w13), None, to_bf16_bits(w2), None
+        if self.cfg.wdtype == "mxfp8":
+            c13, s13 = quantize_weight_mx(w13)
+            c2, s2 = quantize_weight_mx(w2)
+            return c13, s13, c2, s2
         c13, s13 = quantize_weight_block_fp8(w13)
         c2, s2 = quantize_weight_block_fp8(w2)
         return c13, s13, c2, s2

@@ -25,7 +25,10 @@ optimisations for SageMaker AI on H200):
   quant_act    dynamic fp8-e4m3 quantisation with one power-of-two scale per
                row and 128-column group (P2, section 1.2, the fused
                SiLU-mul-quant kernel: amax, floor 1e-10, times 1/448, rounded up
-               to a power of two, divide, clamp to +-448, cast to e4m3).
+               to a power of two, divide, clamp to +-448, cast to e4m3).  The
+               MXFP8 variant (the successor scheme of P3, section on
+               quantisation for Blackwell) uses the same rule on 1x32 groups;
+               its power-of-two scales are E8M0 bytes.
   forward      grouped gate/up GEMM, SiLU-gated multiply with the rounding
                points of P2 section 1.2 (gate/up rounded to the activation dtype,
                SiLU rounded before the multiply, product rounded), optional fp8
@@ -66,6 +69,7 @@ __all__ = [
     "round_bf16", "bf16_bits_to_f64", "round_e4m3", "e4m3_decode",
     "e4m3_encode", "fl32", "pow2_ceil", "fp8_group_scale", "quant_act",
     "route", "align", "align_capacity", "dequant_block", "forward", "expert_rows",
+    "MX_BLOCK", "e8m0_decode", "e8m0_encode", "dequant_mx",
 ]
 
 # ----------------------------------------------------------------------------
@@ -198,6 +202,41 @@ def quant_act(v, group: int = 128):
 
 
 # ----------------------------------------------------------------------------
+# MXFP8 (P3, quantisation section: MXFP8 weights, converted statically):
+# e4m3 elements with one E8M0 scale (a bare power of two) per 1x32 block along
+# the reduction dimension.  Reading: activations (x and the intermediate) are
+# quantised with the P2 section 1.2 rule on 1x32 groups (quant_act(v, 32)),
+# which never saturates; weights arrive already converted by the caller.
+# ----------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def e8m0_decode(s) -> np.ndarray:
+    """E8M0 scale byte -> 2^(s - 127); 255 is NaN."""
+    s = np.asarray(s).astype(np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+
+
+def e8m0_encode(scale) -> np.ndarray:
+    """Power of two in [2^-127, 2^127] -> its E8M0 byte (exact, via frexp)."""
+    m, e = np.frexp(np.asarray(scale, dtype=np.float64))
+    if not np.all(m == 0.5):
+        raise ValueError("E8M0 holds powers of two only")
+    b = e - 1 + 127
+    if np.any((b < 0) | (b > 254)):
+        raise ValueError("power of two outside the E8M0 range")
+    return b.astype(np.uint8)
+
+
+def dequant_mx(codes, scales, block: int = MX_BLOCK) -> np.ndarray:
+    """MXFP8 weights from e4m3 codes [.., N, K] and E8M0 scales [.., N, K/block]:
+    value = e4m3(code) * 2^(s - 127) of its row's K block."""
+    w = e4m3_decode(codes)
+    return w * np.repeat(e8m0_decode(scales), block, axis=-1)
+
+
+# ----------------------------------------------------------------------------
 # Routing: softmax over experts, top-k, renormalise
 # ----------------------------------------------------------------------------
 
@@ -312,7 +351,8 @@ def forward(x, w13, w2, topk_ids, topk_weights, *, mode: str = "method",
     topk_weights [T, k] float
     mode         "method": the rounding points of the fused kernel;
                  "pure": no rounding beyond the inputs
-    fp8          quantise x and the intermediate per row and 128-group
+    fp8          quantise x and the intermediate per row and ``group`` columns
+                 (128: block-scaled fp8; 32: MXFP8)
     """
     if mode not in ("method", "pure"):
         raise ValueError(mode)

@@ -8,7 +8,7 @@ Comparison rules
   * layer output (bf16): the output's own rounding (half a bf16 ulp of the
     unrounded oracle value) is not charged; pass iff
         max_i(|gpu_i - o_i| - ulp_bf16(o_i)/2) <= tau * RMS(o)
-    with tau = 2e-2 for bf16 weights and 6e-2 for fp8, RMS over the compared
+    with tau = 2e-2 for bf16 weights and 6e-2 for fp8 and MXFP8, RMS over the compared
     outputs of the unrounded fp64 oracle.
 """
 from __future__ import annotations
@@ -23,7 +23,7 @@ import oracle as O
 from moe_layer_amd import ops
 from moe_layer_amd.workloads import CONFIGS, Config, Workload
 
-TAU = {"bf16": 2e-2, "fp8": 6e-2}
+TAU = {"bf16": 2e-2, "fp8": 6e-2, "mxfp8": 6e-2}
 
 
 def log(msg: str):
@@ -58,11 +58,16 @@ class DeviceLayer:
             self.w13 = torch.zeros((E, 2 * I, H), dtype=torch.bfloat16, device=d)
             self.w2 = torch.zeros((E, H, I), dtype=torch.bfloat16, device=d)
             self.s13 = self.s2 = None
-        else:
+        elif cfg.wdtype == "fp8":
             self.w13 = torch.zeros((E, 2 * I, H), dtype=torch.uint8, device=d)
             self.w2 = torch.zeros((E, H, I), dtype=torch.uint8, device=d)
             self.s13 = torch.ones((E, 2 * I // 128, H // 128), dtype=torch.float32, device=d)
             self.s2 = torch.ones((E, H // 128, I // 128), dtype=torch.float32, device=d)
+        else:   # mxfp8: E8M0 scale bytes per row and 32 K elements (127 = 1.0)
+            self.w13 = torch.zeros((E, 2 * I, H), dtype=torch.uint8, device=d)
+            self.w2 = torch.zeros((E, H, I), dtype=torch.uint8, device=d)
+            self.s13 = torch.full((E, 2 * I, H // 32), 127, dtype=torch.uint8, device=d)
+            self.s2 = torch.full((E, H, I // 32), 127, dtype=torch.uint8, device=d)
         self.host = {}
 
     def ensure(self, experts):
@@ -92,6 +97,8 @@ class DeviceLayer:
         c13, s13, c2, s2 = self.host[int(e)]
         if self.cfg.wdtype == "bf16":
             return O.bf16_bits_to_f64(c13), O.bf16_bits_to_f64(c2)
+        if self.cfg.wdtype == "mxfp8":
+            return O.dequant_mx(c13, s13), O.dequant_mx(c2, s2)
         return O.dequant_block(c13, s13), O.dequant_block(c2, s2)
 
 
@@ -119,7 +126,8 @@ def routing(cfg: Config):
 def oracle_tokens(layer: DeviceLayer, x64: np.ndarray, ids: np.ndarray, tw: np.ndarray, tokens) -> np.ndarray:
     """Unrounded oracle output rows for the given tokens, one expert at a time."""
     tokens = np.asarray(tokens)
-    fp8 = layer.cfg.wdtype == "fp8"
+    fp8 = layer.cfg.wdtype != "bf16"
+    group = 32 if layer.cfg.wdtype == "mxfp8" else 128
     out = np.zeros((len(tokens), x64.shape[1]))
     slots = [(i, j) for i, t in enumerate(tokens) for j in range(ids.shape[1])]
     by_e = {}
@@ -130,7 +138,8 @@ def oracle_tokens(layer: DeviceLayer, x64: np.ndarray, ids: np.ndarray, tw: np.n
     for e, lst in sorted(by_e.items()):
         w13, w2 = layer.exact(e)
         rows_i = [i for i, _ in lst]
-        y = O.expert_rows(x64, w13, w2, tokens[rows_i], [tw[tokens[i], j] for i, j in lst], fp8=fp8)
+        y = O.expert_rows(x64, w13, w2, tokens[rows_i], [tw[tokens[i], j] for i, j in lst], fp8=fp8,
+                          group=group)
         np.add.at(out, rows_i, y)
     return out
 

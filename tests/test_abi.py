@@ -63,7 +63,7 @@ def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAK
     a = ops.forward_args(None, None, None, None, None, shape=(T, E, H, I, k, wdtype), path=path, block_m=block_m)
     for f in ("x", "w13", "w2", "topk_ids", "topk_weights", "out"):
         setattr(a, f, ptr)
-    if wdtype == ops.MOE_WDTYPE_FP8_E4M3 and scales:
+    if wdtype in (ops.MOE_WDTYPE_FP8_E4M3, ops.MOE_WDTYPE_MXFP8) and scales:
         a.w13_scale = a.w2_scale = FAKE
     return a
 
@@ -74,6 +74,8 @@ def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAK
     (64, 8, 2, 0, 16, ops.MOE_PATH_SMALL_M),        # tiny: 16 rows per expert
     (512, 64, 8, 0, 64, ops.MOE_PATH_SMALL_M),      # 64 rows per expert
     (4096, 128, 8, 0, 256, ops.MOE_PATH_LARGE_M),   # prefill: 256 rows per expert
+    (1024, 256, 8, 2, 32, ops.MOE_PATH_SMALL_M),    # MXFP8: 32 rows per expert
+    (8192, 256, 8, 2, 64, ops.MOE_PATH_SMALL_M),    # MXFP8 has no large-M path
 ])
 def test_plan_block_size(T, E, k, wdtype, expect_bm, expect_path):
     H, I = (4096, 256) if wdtype else (4096, 1536)
@@ -91,6 +93,9 @@ def test_plan_block_size(T, E, k, wdtype, expect_bm, expect_path):
         assert p["off_xq"] >= 0 and p["off_inter_scale"] >= 0
     else:
         assert p["off_xq"] == -1 and p["off_inter_scale"] == -1
+    if wdtype == ops.MOE_WDTYPE_MXFP8:   # one E8M0 byte per 32 elements
+        assert p["off_inter"] - p["off_xs"] >= T * H // 32
+        assert p["off_xs"] - p["off_xq"] >= T * H
 
 
 def test_plan_block_override_and_path():
@@ -136,6 +141,9 @@ def test_plan_large_path_limits():
     (dict(ptr=None), ops.MOE_ERR_INVALID_ARG),
     (dict(ptr=ODD), ops.MOE_ERR_INVALID_ARG),
     (dict(wdtype=1, I=256, scales=False), ops.MOE_ERR_INVALID_ARG),
+    (dict(wdtype=2, I=256, scales=False), ops.MOE_ERR_INVALID_ARG),
+    (dict(H=4032, wdtype=2, I=256), ops.MOE_ERR_UNSUPPORTED),   # MXFP8 needs H % 128 == 0
+    (dict(wdtype=3), ops.MOE_ERR_INVALID_ARG),
 ])
 def test_forward_validation(kw, status):
     a = _args(**kw)
@@ -171,3 +179,7 @@ def test_route_align_quant_validation():
     assert L.moe_quant_act(f, -1, 128, f, f, None) == ops.MOE_ERR_INVALID_ARG
     assert L.moe_quant_act(C.c_void_p(FAKE + 8), 4, 128, f, f, None) == ops.MOE_ERR_INVALID_ARG
     assert L.moe_quant_act(None, 0, 128, None, None, None) == ops.MOE_OK
+    assert L.moe_quant_act_mx(f, 4, 100, f, f, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_act_mx(f, -1, 32, f, f, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_act_mx(C.c_void_p(FAKE + 8), 4, 32, f, f, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_act_mx(None, 0, 32, None, None, None) == ops.MOE_OK

@@ -130,6 +130,23 @@ def test_quant_act_bit_exact():
     np.testing.assert_array_equal(codes.cpu().numpy(), c_o)
 
 
+def test_quant_act_mx_bit_exact():
+    """MXFP8 activation quantisation: e4m3 codes and E8M0 scale bytes of every
+    32-column group equal the oracle's, bit for bit."""
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((200, 512)) * 0.1).astype(np.float32)
+    x[0] = 0.0
+    x[1, :32] *= 1e-6
+    x[2, 32:64] *= 1e4
+    x[3, :32] = 1.75
+    x[5] *= np.repeat(np.exp(rng.uniform(-10, 10, 16)), 32).astype(np.float32)
+    bits = torch.from_numpy(x).to(torch.bfloat16)
+    codes, scales = ops.moe_quant_act_mx(bits.to(dev()))
+    c_o, s_o, _ = O.quant_act(bits.to(torch.float64).numpy(), 32)
+    np.testing.assert_array_equal(scales.cpu().numpy(), O.e8m0_encode(s_o))
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_o)
+
+
 # ----------------------------------------------------------------- forward ---
 
 def _forward_case(cfg, tokens=None, **kw):
@@ -158,7 +175,7 @@ def _forward_case(cfg, tokens=None, **kw):
     return out, ws
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
 @pytest.mark.parametrize("block_m", [0, 16, 32, 64])
 def test_forward_tiny(wdtype, block_m):
     _forward_case(replace(CONFIGS["tiny"], wdtype=wdtype), block_m=block_m)
@@ -170,6 +187,10 @@ def test_forward_decode():
 
 def test_forward_fp8_workload():
     _forward_case(CONFIGS["fp8"])
+
+
+def test_forward_mxfp8_workload():
+    _forward_case(CONFIGS["mxfp8"])
 
 
 def test_forward_prefill_sampled():
@@ -228,12 +249,12 @@ def test_forward_prefill_small_path_sampled():
                   path=ops.MOE_PATH_SMALL_M)
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
 def test_forward_ragged_shapes(wdtype):
     """Odd token counts, an expert count that is not a power of two, H/I at the
     smallest supported multiples, invalid and duplicate ids."""
     from moe_layer_amd.workloads import Config
-    q = 128 if wdtype == "fp8" else 64
+    q = 64 if wdtype == "bf16" else 128
     cfg = Config("ragged", 37, 13, 3 * q, 5 * q if wdtype == "bf16" else 2 * q, 3, wdtype, "given")
     wl = Workload(cfg)
     rng = np.random.default_rng(5)
@@ -254,13 +275,14 @@ def test_forward_ragged_shapes(wdtype):
         assert excess <= TAU[wdtype]
 
 
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
 @pytest.mark.parametrize("H,I", [(8448, 384), (8320, 256)])
-def test_forward_fp8_long_k(H, I):
+def test_forward_fp8_long_k(H, I, wdtype):
     """fp8 with more than 64 K-blocks of 128 (the activation-scale table is
     staged in two chunks), an odd K-block count in GEMM2, and H not a
     multiple of 256 (the narrower GEMM2 tile)."""
     from moe_layer_amd.workloads import Config
-    cfg = Config("fp8_longk", 20, 6, H, I, 2, "fp8", "given")
+    cfg = Config("fp8_longk", 20, 6, H, I, 2, wdtype, "given")
     wl = Workload(cfg)
     rng = np.random.default_rng(H + I)
     ids = np.stack([rng.permutation(6)[:2] for _ in range(20)]).astype(np.int32)
@@ -272,8 +294,8 @@ def test_forward_fp8_long_k(H, I):
         out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=bm)
         gpu = out.to(torch.float64).cpu().numpy()
         excess, raw, _ = compare_output(gpu, o)
-        log(f"fp8 H={H} I={I} bm={bm}: excess/RMS={excess:.3e} raw={raw:.3e}")
-        assert excess <= TAU["fp8"]
+        log(f"{wdtype} H={H} I={I} bm={bm}: excess/RMS={excess:.3e} raw={raw:.3e}")
+        assert excess <= TAU[wdtype]
 
 
 # ------------------------------------------------------ self-consistency ---
@@ -286,7 +308,8 @@ def _layer_inputs(cfg):
     return wl, layer, ids.astype(np.int32), tw.astype(np.float32)
 
 
-@pytest.mark.parametrize("name,wdtype", [("tiny", "bf16"), ("tiny", "fp8"), ("decode", "bf16"), ("fp8", "fp8")])
+@pytest.mark.parametrize("name,wdtype", [("tiny", "bf16"), ("tiny", "fp8"), ("tiny", "mxfp8"), ("decode", "bf16"),
+                                         ("fp8", "fp8"), ("mxfp8", "mxfp8")])
 def test_block_m_invariance_bitwise(name, wdtype):
     """Every output element is accumulated over K in the same order whatever the
     block size, so the output is bit-identical across block_m."""
@@ -301,7 +324,7 @@ def test_block_m_invariance_bitwise(name, wdtype):
             assert torch.equal(out, ref), f"block_m={bm}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp8"])
 def test_token_permutation_equivariance(name):
     cfg = CONFIGS[name]
     wl, layer, ids, tw = _layer_inputs(cfg)
@@ -312,7 +335,7 @@ def test_token_permutation_equivariance(name):
     assert torch.equal(outp, out[torch.from_numpy(p).to(out.device)])
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "fp8", "prefill"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "fp8", "mxfp8", "prefill"])
 def test_determinism_and_poisoned_workspace(name):
     """Two runs agree bitwise, also when the workspace starts as all-NaN bytes:
     no padding row or unwritten workspace value reaches the output."""

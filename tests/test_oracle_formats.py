@@ -171,3 +171,47 @@ def test_dequant_block_layout():
     scales = np.arange(6, dtype=np.float64).reshape(2, 3) + 1
     w = O.dequant_block(codes, scales)
     assert w[0, 0] == 1 and w[127, 127] == 1 and w[128, 0] == 4 and w[255, 383] == 6 and w[0, 200] == 2
+
+
+# ------------------------------------------------------------------- MXFP8 ---
+
+def test_e8m0_spec_values():
+    """E8M0 is a bare biased exponent: 0x7F is 1.0, 0x00 is 2^-127, 0xFE is
+    2^127, 0xFF is NaN (OCP microscaling formats)."""
+    d = O.e8m0_decode(np.array([0x7F, 0x00, 0xFE, 0x80, 0x7E, 0xFF]))
+    assert d[0] == 1.0 and d[1] == 2.0 ** -127 and d[2] == 2.0 ** 127
+    assert d[3] == 2.0 and d[4] == 0.5 and np.isnan(d[5])
+    e = np.arange(-127, 128)
+    codes = O.e8m0_encode(np.ldexp(1.0, e))
+    np.testing.assert_array_equal(codes.astype(np.int64), e + 127)
+    with pytest.raises(ValueError):
+        O.e8m0_encode(np.array([3.0]))
+
+
+def test_dequant_mx_matches_element_loop():
+    rng = np.random.default_rng(4)
+    codes = (rng.integers(0, 256, (6, 96)) & 0x7E).astype(np.uint8)   # finite codes
+    scales = rng.integers(100, 150, (6, 3)).astype(np.uint8)
+    got = O.dequant_mx(codes, scales)
+    for r in range(6):
+        for c in range(96):
+            v = O.e4m3_decode(np.array([codes[r, c]]))[0]
+            assert got[r, c] == v * 2.0 ** (int(scales[r, c // 32]) - 127)
+
+
+def test_quant_act_group32_bound_and_e8m0_scales():
+    """MXFP8 activation groups of 32: the same error bound and scale range as
+    the 128 groups, every scale an E8M0-representable power of two."""
+    rng = np.random.default_rng(10)
+    x = O.round_bf16(rng.standard_normal((32, 256)) * np.exp(rng.uniform(-20, 20, (32, 8)).repeat(32, axis=1)))
+    codes, s, deq = O.quant_act(x, 32)
+    assert s.shape == (32, 8)
+    sf = np.repeat(s, 32, axis=1)
+    err = np.abs(x - deq)
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sf))
+    amax = np.abs(x).reshape(32, 8, 32).max(axis=2)
+    assert np.all(amax / s > 224) and np.all(amax / s <= 448)
+    np.testing.assert_array_equal(O.e8m0_decode(O.e8m0_encode(s)), s)
+    # finer groups never raise the error of a group of 128 that contains them
+    _, _, deq128 = O.quant_act(x, 128)
+    assert np.abs(x - deq).max() <= np.abs(x - deq128).max()

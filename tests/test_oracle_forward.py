@@ -28,7 +28,12 @@ def _bf16(a):
 def _layer(T, E, H, I, k, seed, fp8=False):
     rng = np.random.default_rng(seed)
     x = _bf16(rng.standard_normal((T, H)) * 0.1)
-    if fp8:
+    if fp8 == "mx":
+        w13 = O.dequant_mx(rng.integers(0, 256, (E, 2 * I, H)).astype(np.uint8) & 0x77,
+                           rng.integers(110, 125, (E, 2 * I, H // 32)).astype(np.uint8))
+        w2 = O.dequant_mx(rng.integers(0, 256, (E, H, I)).astype(np.uint8) & 0x77,
+                          rng.integers(110, 125, (E, H, I // 32)).astype(np.uint8))
+    elif fp8:
         w13 = O.dequant_block(rng.integers(0, 256, (E, 2 * I, H)).astype(np.uint8) & 0x77,
                               np.abs(rng.standard_normal((E, 2 * I // 128, H // 128))) * 0.01)
         w2 = O.dequant_block(rng.integers(0, 256, (E, H, I)).astype(np.uint8) & 0x77,
@@ -54,7 +59,7 @@ def test_E1_k1_pure_is_dense_swiglu_mlp():
     np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-14)
 
 
-def _dense_masked(x, w13, w2, ids, tw, method, fp8):
+def _dense_masked(x, w13, w2, ids, tw, method, fp8, group=128):
     """out[t] = sum_e G[t,e] * FFN_e(x_t), G[t,e] = sum of tw[t,j] over j with
     ids[t,j] == e.  Scalar loops over tokens, experts and features."""
     T, H = x.shape
@@ -64,7 +69,7 @@ def _dense_masked(x, w13, w2, ids, tw, method, fp8):
     for t in range(T):
         xt = x[t]
         if fp8 and method:
-            xt = O.quant_act(xt[None, :])[2][0]
+            xt = O.quant_act(xt[None, :], group)[2][0]
         for e in range(E):
             G = sum(tw[t, j] for j in range(ids.shape[1]) if ids[t, j] == e)
             if G == 0:
@@ -80,26 +85,43 @@ def _dense_masked(x, w13, w2, ids, tw, method, fp8):
                 else:
                     act[i] = g / (1.0 + np.exp(-g)) * u
             if fp8 and method:
-                act = O.quant_act(act[None, :])[2][0]
+                act = O.quant_act(act[None, :], group)[2][0]
             for h in range(H):
                 out[t, h] += G * float(np.dot(w2[e, h], act))
     return out
 
 
 @pytest.mark.parametrize("mode", ["method", "pure"])
-@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("fp8", [False, True, "mx"])
 def test_matches_dense_masked_evaluation(mode, fp8):
     if fp8:
         T, E, H, I, k = 5, 3, 128, 128, 2
     else:
         T, E, H, I, k = 6, 4, 24, 16, 3
-    x, w13, w2, ids, tw = _layer(T, E, H, I, k, 1 + fp8, fp8)
+    group = 32 if fp8 == "mx" else 128
+    x, w13, w2, ids, tw = _layer(T, E, H, I, k, 1 + bool(fp8), fp8)
     ids[0, 1] = ids[0, 0]          # a duplicate id
     ids[1, 0] = -1                 # an id outside [0, E): not routed
     ids[2, 1] = E
-    got = O.forward(x, w13, w2, ids, tw, mode=mode, fp8=fp8)
-    ref = _dense_masked(x, w13, w2, ids, tw, mode == "method", fp8)
+    got = O.forward(x, w13, w2, ids, tw, mode=mode, fp8=bool(fp8), group=group)
+    ref = _dense_masked(x, w13, w2, ids, tw, mode == "method", bool(fp8), group)
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_mx_groups_quantise_the_intermediate_per_32_columns():
+    """Hand-derived: one token, one expert, I = 64.  The intermediate's two
+    32-column groups get their own scales: a group of 1.5 values quantises
+    exactly, a group whose max is 3.0 maps 3.0 to 384 * 2^-7."""
+    H, I = 32, 64
+    x = np.zeros((1, H)); x[0, 0] = 1.0
+    w13 = np.zeros((1, 2 * I, H))
+    w13[0, :I, 0] = 30.0           # gate: silu(30) rounds to 30 in bf16
+    w13[0, I:I + 32, 0] = 0.05     # up, group 0: a = bf16(30 * 0.05) = 1.5
+    w13[0, I + 32:, 0] = 0.1       # up, group 1: a = 3.0
+    w2 = np.zeros((1, H, I)); w2[0, 0, :] = 1.0
+    out = O.forward(x, w13, w2, np.array([[0]]), np.array([[1.0]]), fp8=True, group=32)
+    # group scales: pow2ceil(1.5/448) = 2^-8 (1.5 -> 384 exactly), pow2ceil(3/448) = 2^-7
+    assert out[0, 0] == 32 * 1.5 + 32 * 3.0
 
 
 @pytest.mark.parametrize("case", [c for c in GOLDEN["forward"] if not c["fp8"]])
