@@ -231,7 +231,8 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  *              256-byte aligned; its contents on entry do not matter and on
  *              exit hold the intermediates (layout in moe_plan_info).
  * Limits: bf16 requires H % 64 == 0 and I % 64 == 0; fp8 and MXFP8 require
- * H % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED).  The large-M
+ * H % 128 == 0 and I % 128 == 0; MXFP8 also T * H < 2^32 (else
+ * MOE_ERR_UNSUPPORTED).  The large-M
  * path needs bf16 weights, H % 256 == 0 and I % 128 == 0; AUTO takes it from
  * 96 routed rows per expert on, forcing it elsewhere is MOE_ERR_UNSUPPORTED.
  * The workspace's activation scales (off_xs, off_inter_scale) are fp32 for

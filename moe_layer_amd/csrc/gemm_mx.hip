@@ -17,8 +17,7 @@
 // rounding points (P2 section 1.2) and re-quantises the intermediate per row
 // and 32-column group (E8M0 scale + e4m3 codes, group amax exchanged through
 // LDS); GEMM2's multiplies by the router weight in fp32 and writes y by flat
-// slot.  Weight scales are read per lane (one byte per tile and step); the
-// activation scales of the block's rows are staged in LDS per workgroup.
+// slot.
 #include "common.h"
 
 namespace moe {
@@ -46,25 +45,38 @@ struct MxStage {
     uint32_t sb[U][NT];   // E8M0 byte of the lane's token row and K block
 };
 
-// ap/bp: the lane's first byte of step 0 (K offset 16 * (l / 16)); asp: the lane's weight-scale
-// byte of step 0 (advances 4 bytes a step); bsp: the lane's byte in the LDS
-// table (advances 4 bytes a step).
+// Operand addressing: a wave-uniform base per weight tile (scalar registers)
+// plus one 32-bit lane offset shared by all weight tiles, so the loads take
+// the scalar-base + vector-offset form and few vector registers hold
+// addresses.  Tokens: one uniform base plus a 32-bit offset per token tile.
+// Weight scales are read per lane (one byte per tile and step; staging them
+// in LDS as well measured no faster); the tokens' scales come from an LDS
+// table the workgroup fills per chunk of kTabSteps steps.
+template <int MT, int NT>
+struct MxAddr {
+    const uint8_t* a[MT];    // weight tile bases (uniform)
+    const uint8_t* as[MT];   // weight-scale tile bases (uniform)
+    uint32_t aoff;           // lane offset into a weight tile, step 0
+    uint32_t asoff;          // lane offset into a weight-scale tile, step 0
+    const uint8_t* b;        // token operand base (uniform)
+    uint32_t boff[NT];       // lane offset of each token tile, step 0
+    const uint8_t* bs[NT];   // the lane's byte in the LDS token-scale table, step 0
+};
+
 template <int MT, int NT, int U>
-__device__ __forceinline__ void mx_load(MxStage<MT, NT, U>& st, const uint8_t* const (&ap)[MT],
-                                        const uint8_t* const (&bp)[NT], const uint8_t* const (&asp)[MT],
-                                        const uint8_t* const (&bsp)[NT], int step0) {
+__device__ __forceinline__ void mx_load(MxStage<MT, NT, U>& st, const MxAddr<MT, NT>& ad, int step0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t off = int64_t(step0 + u) * kStepK;
+        const uint32_t off = uint32_t(step0 + u) * kStepK;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            st.a[u][m] = ld32(ap[m] + off);
-            st.sa[u][m] = asp[m][4 * (step0 + u)];
+            st.a[u][m] = ld32(ad.a[m] + (ad.aoff + off));
+            st.sa[u][m] = ad.as[m][ad.asoff + 4 * (step0 + u)];
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            st.b[u][n] = ld32(bp[n] + off);
-            st.sb[u][n] = bsp[n][4 * (step0 + u)];
+            st.b[u][n] = ld32(ad.b + (ad.boff[n] + off));
+            st.sb[u][n] = ad.bs[n][4 * (step0 + u)];
         }
     }
 }
@@ -83,28 +95,32 @@ __device__ __forceinline__ void mx_compute(const MxStage<MT, NT, U>& st, f32x4 (
 
 // K loop over nsteps steps, two register stages (the block-fp8 kernels' loop).
 template <int MT, int NT, int U>
-__device__ __forceinline__ void mx_mainloop(const uint8_t* const (&ap)[MT], const uint8_t* const (&bp)[NT],
-                                            const uint8_t* const (&asp)[MT], const uint8_t* const (&bsp)[NT],
-                                            int nsteps, f32x4 (&acc)[MT][NT]) {
+__device__ __forceinline__ void mx_mainloop(const MxAddr<MT, NT>& ad, int nsteps, f32x4 (&acc)[MT][NT]) {
     MxStage<MT, NT, U> s0, s1;
-    mx_load<MT, NT, U>(s0, ap, bp, asp, bsp, 0);
+    mx_load<MT, NT, U>(s0, ad, 0);
     for (int k = 0; k < nsteps; k += 2 * U) {
         const bool has1 = k + U < nsteps;
-        if (has1) mx_load<MT, NT, U>(s1, ap, bp, asp, bsp, k + U);
+        if (has1) mx_load<MT, NT, U>(s1, ad, k + U);
         mx_compute<MT, NT, U>(s0, acc);
-        if (k + 2 * U < nsteps) mx_load<MT, NT, U>(s0, ap, bp, asp, bsp, k + 2 * U);
+        if (k + 2 * U < nsteps) mx_load<MT, NT, U>(s0, ad, k + 2 * U);
         if (has1) mx_compute<MT, NT, U>(s1, acc);
     }
 }
 
-// Per chunk of kTabSteps K steps: stage the BM rows' activation-scale bytes
+// Per chunk of kTabSteps K steps: stage the BM token rows' scale bytes
 // (row_scale(r) points at row r's first byte) in LDS, then run the K loop.
 template <int MT, int NT, int BM, int NTHREADS, typename RowScale>
-__device__ __forceinline__ void mx_kloop(const uint8_t* const (&ap)[MT], const uint8_t* const (&bp)[NT],
-                                         const uint8_t* const (&asp)[MT], RowScale row_scale, int nsteps,
-                                         uint8_t* tab, f32x4 (&acc)[MT][NT]) {
+__device__ __forceinline__ void mx_kloop(MxAddr<MT, NT> ad, RowScale row_scale, int nsteps, uint8_t* tab,
+                                         f32x4 (&acc)[MT][NT]) {
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15, lk = lane >> 4;
+    const uint32_t aoff0 = ad.aoff, asoff0 = ad.asoff;
+    uint32_t boff0[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        boff0[n] = ad.boff[n];
+        ad.bs[n] = tab + (n * 16 + lr) * kTabStride + lk;
+    }
     for (int c0 = 0; c0 < nsteps; c0 += kTabSteps) {
         const int cs = min(kTabSteps, nsteps - c0);
         __syncthreads();   // the previous chunk's table reads are done
@@ -114,21 +130,11 @@ __device__ __forceinline__ void mx_kloop(const uint8_t* const (&ap)[MT], const u
                 *reinterpret_cast<const uint32_t*>(row_scale(r) + 4 * (c0 + k));
         }
         __syncthreads();
-        const uint8_t* apc[MT];
-        const uint8_t* aspc[MT];
-        const uint8_t* bpc[NT];
-        const uint8_t* bspc[NT];
+        ad.aoff = aoff0 + uint32_t(c0) * kStepK;
+        ad.asoff = asoff0 + 4 * c0;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            apc[m] = ap[m] + int64_t(c0) * kStepK;
-            aspc[m] = asp[m] + 4 * c0;
-        }
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            bpc[n] = bp[n] + int64_t(c0) * kStepK;
-            bspc[n] = tab + (n * 16 + lr) * kTabStride + lk;
-        }
-        mx_mainloop<MT, NT, 1>(apc, bpc, aspc, bspc, cs, acc);
+        for (int n = 0; n < NT; ++n) ad.boff[n] = boff0[n] + uint32_t(c0) * kStepK;
+        mx_mainloop<MT, NT, 1>(ad, cs, acc);
     }
 }
 
@@ -157,21 +163,22 @@ __global__ __launch_bounds__(NW * 64) void gemm1_mx_kernel(GemmArgs g, int ntile
 
     const uint8_t* w13 = static_cast<const uint8_t*>(g.w13);
     const uint8_t* w13s = static_cast<const uint8_t*>(g.w13_scale);
-    const uint8_t* ap[MT];
-    const uint8_t* asp[MT];
-    const uint8_t* bp[NT];
+    MxAddr<MT, NT> ad;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        const int64_t row = int64_t(e) * 2 * I + (m < WT ? i0 + m * 16 : I + i0 + (m - WT) * 16) + lr;
-        ap[m] = w13 + row * H + lk * 16;
-        asp[m] = w13s + row * kbh + lk;
+        const int64_t row0 = int64_t(e) * 2 * I + (m < WT ? i0 + m * 16 : I + i0 + (m - WT) * 16);
+        ad.a[m] = w13 + row0 * H;
+        ad.as[m] = w13s + row0 * kbh;
     }
+    ad.aoff = uint32_t(lr * H + lk * 16);
+    ad.asoff = uint32_t(lr * kbh + lk);
+    ad.b = g.xq;
     const int32_t* rows = g.sorted_ids + blk * BM;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const int f = rows[n * 16 + lr];
         const int tok = f < R ? f / g.topk : 0;   // padding rows read token 0, never stored as real rows
-        bp[n] = g.xq + int64_t(tok) * H + lk * 16;
+        ad.boff[n] = uint32_t(tok) * uint32_t(H) + uint32_t(lk * 16);
     }
 
     f32x4 acc[MT][NT];
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(NW * 64) void gemm1_mx_kernel(GemmArgs g, int ntile
         const int f = rows[r];
         return xs + int64_t(f < R ? f / g.topk : 0) * kbh;
     };
-    mx_kloop<MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, H / kStepK, tab, acc);
+    mx_kloop<MT, NT, BM, NW * 64>(ad, row_scale, H / kStepK, tab, acc);
 
     // epilogue: a = silu(g) * u with the bf16 rounding points
     float a[WT][NT][4];
@@ -261,18 +268,18 @@ __global__ __launch_bounds__(NW * 64) void gemm2_mx_kernel(GemmArgs g, int ntile
 
     const uint8_t* w2 = static_cast<const uint8_t*>(g.w2);
     const uint8_t* w2s = static_cast<const uint8_t*>(g.w2_scale);
-    const uint8_t* inter = static_cast<const uint8_t*>(g.inter);
-    const uint8_t* ap[MT];
-    const uint8_t* asp[MT];
-    const uint8_t* bp[NT];
+    MxAddr<MT, NT> ad;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        const int64_t row = int64_t(e) * H + h0 + m * 16 + lr;
-        ap[m] = w2 + row * I + lk * 16;
-        asp[m] = w2s + row * kbi + lk;
+        const int64_t row0 = int64_t(e) * H + h0 + m * 16;
+        ad.a[m] = w2 + row0 * I;
+        ad.as[m] = w2s + row0 * kbi;
     }
+    ad.aoff = uint32_t(lr * I + lk * 16);
+    ad.asoff = uint32_t(lr * kbi + lk);
+    ad.b = static_cast<const uint8_t*>(g.inter) + int64_t(blk) * BM * I;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) bp[n] = inter + int64_t(blk * BM + n * 16 + lr) * I + lk * 16;
+    for (int n = 0; n < NT; ++n) ad.boff[n] = uint32_t((n * 16 + lr) * I + lk * 16);
 
     f32x4 acc[MT][NT];
 #pragma unroll
@@ -282,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void gemm2_mx_kernel(GemmArgs g, int ntile
     __shared__ __attribute__((aligned(16))) uint8_t tab[BM * kTabStride];
     const uint8_t* scales = reinterpret_cast<const uint8_t*>(g.inter_scale) + int64_t(blk) * BM * kbi;
     auto row_scale = [&](int r) { return scales + int64_t(r) * kbi; };
-    mx_kloop<MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, I / kStepK, tab, acc);
+    mx_kloop<MT, NT, BM, NW * 64>(ad, row_scale, I / kStepK, tab, acc);
 
 #pragma unroll
     for (int n = 0; n < NT; ++n) {

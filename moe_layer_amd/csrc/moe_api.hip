@@ -47,6 +47,8 @@ int validate_forward_scalars(const moe_forward_args* a) {
     const int q = a->wdtype == MOE_WDTYPE_BF16 ? 64 : MOE_QUANT_GROUP;
     if (a->H % q != 0 || a->I % q != 0) return MOE_ERR_UNSUPPORTED;
     if (int64_t(a->T) * a->topk > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    // the MXFP8 kernels address the quantised activations with 32-bit offsets
+    if (a->wdtype == MOE_WDTYPE_MXFP8 && int64_t(a->T) * a->H >= (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 

@@ -144,6 +144,7 @@ def test_plan_large_path_limits():
     (dict(wdtype=2, I=256, scales=False), ops.MOE_ERR_INVALID_ARG),
     (dict(H=4032, wdtype=2, I=256), ops.MOE_ERR_UNSUPPORTED),   # MXFP8 needs H % 128 == 0
     (dict(wdtype=3), ops.MOE_ERR_INVALID_ARG),
+    (dict(T=1 << 20, H=4096, I=256, wdtype=2), ops.MOE_ERR_UNSUPPORTED),   # MXFP8: T * H < 2^32
 ])
 def test_forward_validation(kw, status):
     a = _args(**kw)
