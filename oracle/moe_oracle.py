@@ -52,7 +52,12 @@ path must follow):
   * the power-of-two scale is the smallest power of two >= the fp32 product,
     computed exactly (never through an approximate log2);
   * fp8 is OCP E4M3FN (max 448, no infinities), round to nearest even;
-  * the layer output is returned in fp64, unrounded.
+  * the layer output is returned in fp64, unrounded;
+  * layer variants (P2 section 1.1 names both switches, nothing more):
+    with the router weight on the input, the token's (quantised) input row is
+    multiplied by the slot's weight before the gate/up GEMM and the down GEMM
+    output is not weighted; a SwiGLU clamp limit L caps the gate at L and
+    holds the up value to [-L, L], after their bf16 rounding.
 
 Every input of the method is exact in fp64: bf16 values and e4m3 codes times
 fp32 block scales promote without error, so the oracle and the GPU consume the
@@ -326,20 +331,27 @@ def dequant_block(codes, scales, block: int = 128) -> np.ndarray:
     return w * s
 
 
-def _silu_mul(g, u, method: bool):
+def _silu_mul(g, u, method: bool, clamp_limit=None):
     """SiLU(gate) * up; in method mode with the rounding points of the fused
     kernel: gate/up in bf16, SiLU rounded to bf16 before the multiply, product
-    rounded to bf16."""
+    rounded to bf16.  With a clamp limit L (the activation config's
+    ``clamp_limit``, P2 section 1.1), the gate is capped at L and the up value
+    held to [-L, L] (after their bf16 rounding in method mode)."""
     if method:
         g = round_bf16(g)
         u = round_bf16(u)
+    if clamp_limit is not None:
+        g = np.minimum(g, clamp_limit)
+        u = np.clip(u, -clamp_limit, clamp_limit)
+    if method:
         s = round_bf16(g / (1.0 + np.exp(-g)))
         return round_bf16(s * u)
     return g / (1.0 + np.exp(-g)) * u
 
 
 def forward(x, w13, w2, topk_ids, topk_weights, *, mode: str = "method",
-            fp8: bool = False, group: int = 128):
+            fp8: bool = False, group: int = 128, weight_on_input: bool = False,
+            clamp_limit=None):
     """The layer output out[t] = sum_j tw[t,j] * W2[e] . act(W13[e] . x_t) for
     the valid experts e = topk_ids[t, j], returned unrounded in fp64.
 
@@ -353,6 +365,12 @@ def forward(x, w13, w2, topk_ids, topk_weights, *, mode: str = "method",
                  "pure": no rounding beyond the inputs
     fp8          quantise x and the intermediate per row and ``group`` columns
                  (128: block-scaled fp8; 32: MXFP8)
+    weight_on_input
+                 apply the router weight to the token's input row before the
+                 gate/up GEMM instead of after the down GEMM (P2 section 1.1,
+                 ``apply_router_weight_on_input``); the input is the quantised
+                 row when fp8, and the scaled row itself is not rounded
+    clamp_limit  None, or the SwiGLU clamp limit L > 0 (see ``_silu_mul``)
     """
     if mode not in ("method", "pure"):
         raise ValueError(mode)
@@ -374,29 +392,36 @@ def forward(x, w13, w2, topk_ids, topk_weights, *, mode: str = "method",
         if slots.size == 0:
             continue
         tok = slots // k
-        h = xh[tok] @ np.asarray(w13[e], dtype=np.float64).T        # [rows, 2I]
-        a = _silu_mul(h[:, :I], h[:, I:], method)
+        w_rows = tw.reshape(-1)[slots][:, None]
+        xin = xh[tok] * w_rows if weight_on_input else xh[tok]
+        h = xin @ np.asarray(w13[e], dtype=np.float64).T             # [rows, 2I]
+        a = _silu_mul(h[:, :I], h[:, I:], method, clamp_limit)
         if fp8 and method:
             a = quant_act(a, group)[2]
         y = a @ np.asarray(w2[e], dtype=np.float64).T                # [rows, H]
-        y *= tw.reshape(-1)[slots][:, None]
+        if not weight_on_input:
+            y *= w_rows
         np.add.at(out, tok, y)
     return out
 
 
 def expert_rows(x, w13_e, w2_e, rows_tok, rows_tw, *, mode="method", fp8=False,
-                group: int = 128):
+                group: int = 128, weight_on_input: bool = False, clamp_limit=None):
     """Contribution y = tw * W2[e] . act(W13[e] . x_t) of one expert to the
     given tokens (used to evaluate sampled outputs of large layers one expert
-    at a time).  Returns [len(rows_tok), H] fp64."""
+    at a time), with the options of ``forward``.  Returns [len(rows_tok), H]
+    fp64."""
     method = mode == "method"
     xt = np.asarray(x, dtype=np.float64)[rows_tok]
     if fp8 and method:
         xt = quant_act(xt, group)[2]
+    w_rows = np.asarray(rows_tw, dtype=np.float64)[:, None]
+    if weight_on_input:
+        xt = xt * w_rows
     I = w13_e.shape[0] // 2
     h = xt @ np.asarray(w13_e, dtype=np.float64).T
-    a = _silu_mul(h[:, :I], h[:, I:], method)
+    a = _silu_mul(h[:, :I], h[:, I:], method, clamp_limit)
     if fp8 and method:
         a = quant_act(a, group)[2]
     y = a @ np.asarray(w2_e, dtype=np.float64).T
-    return y * np.asarray(rows_tw, dtype=np.float64)[:, None]
+    return y if weight_on_input else y * w_rows

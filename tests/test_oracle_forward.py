@@ -7,7 +7,10 @@
   gather), agrees in both modes, bf16 and fp8, with duplicate and invalid ids;
 * hand-derived worked examples pin the rounding points;
 * invariants: linear in the router weights, token-permutation equivariant,
-  zero weights give zero, a duplicated id equals the summed weight.
+  zero weights give zero, a duplicated id equals the summed weight;
+* the layer variants (router weight on the input, SwiGLU clamp limit) against
+  slot-by-slot scalar loops, a dense MLP of the scaled input, hand-derived
+  examples and their special cases (unit weights, a limit nothing reaches).
 """
 import json
 import os
@@ -189,3 +192,134 @@ def test_method_differs_from_pure_by_rounding_only():
     p = O.forward(x, w13, w2, ids, tw, mode="pure")
     rms = np.sqrt(np.mean(p ** 2))
     assert 0 < np.max(np.abs(m - p)) < 0.05 * rms
+
+
+# ---------------------------------------------------------------------------
+# layer variants: router weight on the input, SwiGLU clamp limit
+# ---------------------------------------------------------------------------
+
+def _per_slot_loops(x, w13, w2, ids, tw, method, fp8, group=128, weight_on_input=False, clamp_limit=None):
+    """out[t] = sum_j FFN_{ids[t,j]}(x_t, tw[t,j]) slot by slot with scalar
+    loops over features (a different algorithm from the oracle's per-expert
+    gather).  The variants are written out inline."""
+    T, H = x.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    out = np.zeros((T, H))
+    for t in range(T):
+        xq = x[t]
+        if fp8 and method:
+            xq = O.quant_act(xq[None, :], group)[2][0]
+        for j in range(ids.shape[1]):
+            e = ids[t, j]
+            if not 0 <= e < E:
+                continue
+            xin = xq * tw[t, j] if weight_on_input else xq
+            act = np.empty(I)
+            for i in range(I):
+                g = float(np.dot(w13[e, i], xin))
+                u = float(np.dot(w13[e, I + i], xin))
+                if method:
+                    g, u = _bf16(g)[()], _bf16(u)[()]
+                if clamp_limit is not None:
+                    g = min(g, clamp_limit)
+                    u = max(-clamp_limit, min(u, clamp_limit))
+                s = g / (1.0 + np.exp(-g))
+                act[i] = _bf16(_bf16(s)[()] * u)[()] if method else s * u
+            if fp8 and method:
+                act = O.quant_act(act[None, :], group)[2][0]
+            scale = 1.0 if weight_on_input else tw[t, j]
+            for h in range(H):
+                out[t, h] += scale * float(np.dot(w2[e, h], act))
+    return out
+
+
+@pytest.mark.parametrize("mode", ["method", "pure"])
+@pytest.mark.parametrize("fp8", [False, True, "mx"])
+@pytest.mark.parametrize("variant", ["on_input", "clamp", "both"])
+def test_variants_match_per_slot_loops(mode, fp8, variant):
+    if fp8:
+        T, E, H, I, k = 4, 3, 128, 128, 2
+    else:
+        T, E, H, I, k = 6, 4, 24, 16, 3
+    group = 32 if fp8 == "mx" else 128
+    x, w13, w2, ids, tw = _layer(T, E, H, I, k, 21 + bool(fp8), fp8)
+    x = x * 30.0                   # gate/up values well past the clamp limit
+    ids[0, 1] = ids[0, 0]          # a duplicate id
+    ids[1, 0] = -1                 # not routed
+    on_input = variant in ("on_input", "both")
+    limit = 0.7 if variant in ("clamp", "both") else None   # not a bf16 value: rounding comes first
+    got = O.forward(x, w13, w2, ids, tw, mode=mode, fp8=bool(fp8), group=group,
+                    weight_on_input=on_input, clamp_limit=limit)
+    ref = _per_slot_loops(x, w13, w2, ids, tw, mode == "method", bool(fp8), group, on_input, limit)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    if limit is not None:          # the clamp is active in this draw
+        assert not np.allclose(got, O.forward(x, w13, w2, ids, tw, mode=mode, fp8=bool(fp8), group=group,
+                                              weight_on_input=on_input))
+
+
+def test_weight_on_input_E1_k1_pure_is_dense_mlp_of_scaled_input():
+    x, w13, w2, _, _ = _layer(7, 1, 64, 48, 1, 3)
+    ids = np.zeros((7, 1), dtype=np.int64)
+    tw = np.random.default_rng(4).random((7, 1))
+    got = O.forward(x, w13, w2, ids, tw, mode="pure", weight_on_input=True)
+    xt = torch.from_numpy(x * tw)
+    gate, up, down = (torch.from_numpy(a) for a in (w13[0, :48], w13[0, 48:], w2[0]))
+    ref = (torch.nn.functional.silu(xt @ gate.T) * (xt @ up.T)) @ down.T
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_weight_on_input_worked_example():
+    """Hand-derived: x = 1, gate weight 2, up weight 3, router weight 0.5.
+    On the input: g = 1, u = 1.5; silu(1) = 0.7310586 -> bf16 0.73046875;
+    0.73046875 * 1.5 = 1.095703125 -> bf16 (step 2^-7) 1.09375; no weight after
+    the down GEMM.  After the down GEMM instead: g = 2, u = 3; silu(2) =
+    1.7615942 -> 1.7578125; * 3 = 5.2734375 -> (step 2^-5) 5.28125; * 0.5."""
+    x = np.array([[1.0]])
+    w13 = np.array([[[2.0], [3.0]]])
+    w2 = np.array([[[1.0]]])
+    ids, tw = np.array([[0]]), np.array([[0.5]])
+    assert O.forward(x, w13, w2, ids, tw, weight_on_input=True)[0, 0] == 1.09375
+    assert O.forward(x, w13, w2, ids, tw)[0, 0] == 0.5 * 5.28125
+
+
+def test_clamp_worked_examples():
+    """Hand-derived, L = 7, x = 1, one expert, down weight 1.
+    gate 10, up 20: both clamp to 7; silu(7) = 6.99363 -> bf16 (step 2^-5)
+    7.0; a = 49.  Without the limit: silu(10) = 9.99955 -> (step 2^-4) 10.0,
+    a = 200.  gate 10, up -20: a = -49.  gate -10 stays -10 (the gate is capped
+    from above only): silu(-10) = -4.5397869e-4 -> bf16 (step 2^-19)
+    -238 * 2^-19; times up 2 -> -238 * 2^-18, exact in bf16."""
+    def one(gv, uv, limit):
+        w13 = np.array([[[gv], [uv]]])
+        return O.forward(np.array([[1.0]]), w13, np.array([[[1.0]]]), np.array([[0]]),
+                         np.array([[1.0]]), clamp_limit=limit)[0, 0]
+    assert one(10.0, 20.0, 7.0) == 49.0
+    assert one(10.0, 20.0, None) == 200.0
+    assert one(10.0, -20.0, 7.0) == -49.0
+    assert one(-10.0, 2.0, 7.0) == -238 * 2.0 ** -18
+
+
+def test_variant_special_cases():
+    T, E, H, I, k = 8, 4, 32, 16, 2
+    x, w13, w2, ids, tw = _layer(T, E, H, I, k, 31)
+    base = O.forward(x, w13, w2, ids, tw)
+    # unit router weights: the weight's position does not matter
+    ones = np.ones_like(tw)
+    np.testing.assert_array_equal(O.forward(x, w13, w2, ids, ones, weight_on_input=True),
+                                  O.forward(x, w13, w2, ids, ones))
+    # a limit beyond every gate/up value changes nothing
+    np.testing.assert_array_equal(O.forward(x, w13, w2, ids, tw, clamp_limit=1e30), base)
+    # with the weight on the input the layer is no longer linear in the weights
+    assert not np.allclose(O.forward(x, w13, w2, ids, 2 * tw, weight_on_input=True),
+                           2 * O.forward(x, w13, w2, ids, tw, weight_on_input=True))
+    # expert_rows follows the same options
+    for on_input, limit in ((True, None), (False, 0.05), (True, 0.05)):
+        full = O.forward(x, w13, w2, ids, tw, weight_on_input=on_input, clamp_limit=limit)
+        acc = np.zeros_like(full)
+        for t in range(T):
+            for j in range(k):
+                e = ids[t, j]
+                acc[t] += O.expert_rows(x, w13[e], w2[e], [t], [tw[t, j]], weight_on_input=on_input,
+                                        clamp_limit=limit)[0]
+        np.testing.assert_allclose(acc, full, rtol=1e-12, atol=1e-14)
