@@ -60,6 +60,9 @@ extern "C" {
 #define MOE_PATH_SMALL_M     1   /* weight-streaming path: few rows per expert (decode) */
 #define MOE_PATH_LARGE_M     2   /* LDS-tiled path: many rows per expert (prefill) */
 
+/* layer variants (moe_forward_args.flags) */
+#define MOE_FLAG_WEIGHT_ON_INPUT 1   /* router weight on GEMM1's input, none after GEMM2 */
+
 /* limits */
 #define MOE_MAX_EXPERTS      1024
 #define MOE_MAX_TOPK         64
@@ -186,6 +189,9 @@ typedef struct moe_forward_args {
     int32_t path;         /* MOE_PATH_*; AUTO unless a test forces a path */
     int32_t block_m;      /* rows per expert block; 0 lets the planner choose;
                              small-M path: 16, 32 or 64; large-M path: 256 */
+    int32_t flags;        /* MOE_FLAG_* bits; 0 is the layer of the pages' test */
+    float clamp_limit;    /* SwiGLU clamp limit L: 0 for none, else L > 0
+                             (+inf allowed, the same as none) */
 } moe_forward_args;
 
 /* What moe_forward will do for a set of arguments (the test spy). */
@@ -226,6 +232,15 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  * scaled by its two E8M0 scales inside the matrix-core instruction.
  * fp8 and MXFP8 weights arrive pre-quantised with their scales; the library
  * never quantises weights.
+ * Layer variants (P2 section 1.1 names both switches: the
+ * apply_router_weight_on_input argument and the activation config's clamp
+ * limit):
+ *   MOE_FLAG_WEIGHT_ON_INPUT  the slot's router weight scales the token's
+ *       (quantised) input row of GEMM1 instead of GEMM2's output; GEMM1 being
+ *       linear in that row, it is applied to GEMM1's fp32 accumulator before
+ *       the bf16 rounding of h, and GEMM2's rows are left unweighted;
+ *   clamp_limit L > 0  after their bf16 rounding the gate is capped at L and
+ *       the up value held to [-L, L] before the SiLU-gated multiply.
  *
  *   workspace  device buffer of at least moe_forward_workspace(a) bytes,
  *              256-byte aligned; its contents on entry do not matter and on
@@ -236,7 +251,8 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  * path needs bf16 weights, H % 256 == 0 and I % 128 == 0; AUTO takes it from
  * 96 routed rows per expert on, forcing it elsewhere is MOE_ERR_UNSUPPORTED.
  * The workspace's activation scales (off_xs, off_inter_scale) are fp32 for
- * FP8_E4M3 and E8M0 bytes for MXFP8.
+ * FP8_E4M3 and E8M0 bytes for MXFP8.  Unknown flag bits, and a clamp limit
+ * that is negative or NaN, are MOE_ERR_INVALID_ARG.
  */
 MOE_API int moe_forward(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
                         hipStream_t stream);

@@ -16,6 +16,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;   // 32x32 accumulato
 typedef __attribute__((ext_vector_type(8))) int i32x8;       // 16x16x128 fp8 operand (32 bytes)
 typedef __attribute__((ext_vector_type(4))) int i32x4;       // 16-byte load
 typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kWave = 64;
 constexpr int kGroup = 128;   // fp8 activation group / weight block edge
@@ -66,6 +67,26 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
     return (c & 0x80u) ? -a : a;
 }
 
+// Eight E4M3FN bytes (little-endian in two words) to the bf16 operand of a
+// 16x16x32 bf16 MFMA lane, element i = byte i, each value code * scale.  For a
+// power-of-two scale the result is exact while it stays within bf16's normal
+// range (an e4m3 value has 4 significant bits).  gfx950 converts two bytes per
+// instruction (checked on all 256 codes); the pairs are moved as whole words
+// (element access on bf16 vectors compiled to wrong lane moves).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(int lo, int hi, float scale) {
+    const int w0 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false));
+    const int w1 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true));
+    const int w2 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false));
+    const int w3 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true));
+    return __builtin_bit_cast(bf16x8, i32x4{w0, w1, w2, w3});
+}
+
+// The value of an E8M0 scale byte as fp32: 2^(b - 127) (b = 0 is the fp32
+// subnormal 2^-127; 255, the format's NaN, gives infinity).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    return __uint_as_float(b ? b << 23 : 0x00400000u);
+}
+
 // Smallest power of two >= s for a positive normal fp32 s, exact.
 __device__ __forceinline__ float pow2_ceil(float s) {
     uint32_t u = __float_as_uint(s);
@@ -93,6 +114,21 @@ __device__ __forceinline__ float silu_mul_bf16(float g, float u) {
     const float e = expf(-g);
     const float s = round_bf16(__fdiv_rn(g, __fadd_rn(1.0f, e)));
     return round_bf16(__fmul_rn(s, u));
+}
+
+// The gate/up pair entering the SiLU-gated multiply.  w_in multiplies the
+// fp32 GEMM1 results first (the row's router weight when it applies to the
+// input, which GEMM1 is linear in; else 1, an exact no-op); then the bf16
+// rounding points; then, with a clamp limit, the gate is capped at L and the
+// up value held to [-L, L].
+__device__ __forceinline__ float swiglu_bf16(float hg, float hu, float w_in, bool clamp, float L) {
+    float gv = round_bf16(__fmul_rn(hg, w_in));
+    float uv = round_bf16(__fmul_rn(hu, w_in));
+    if (clamp) {
+        gv = fminf(gv, L);
+        uv = fminf(fmaxf(uv, -L), L);
+    }
+    return silu_mul_bf16(gv, uv);
 }
 
 // ---------------------------------------------------------------------------
@@ -147,7 +183,21 @@ struct GemmArgs {
     void* inter;                // bf16 or fp8 [cap, I]
     float* inter_scale;         // fp32 [cap, I/128] (fp8) or E8M0 bytes [cap, I/32] (MXFP8)
     float* y;                   // fp32 [T*topk, H]
+    int weight_on_input;        // router weight on GEMM1's input instead of GEMM2's output
+    int clamp;                  // SwiGLU clamp on (limit clamp_limit)
+    float clamp_limit;
 };
+
+// Router weight a GEMM1 epilogue applies to sorted slot f (1 unless the
+// weight goes on the input; 0 for padding rows, which are never stored as
+// real rows), and the one GEMM2's epilogue applies.
+__device__ __forceinline__ float gemm1_row_weight(const GemmArgs& g, int f) {
+    if (!g.weight_on_input) return 1.0f;
+    return f < g.T * g.topk ? g.topk_weights[f] : 0.0f;
+}
+__device__ __forceinline__ float gemm2_row_weight(const GemmArgs& g, int f) {
+    return g.weight_on_input ? 1.0f : g.topk_weights[f];
+}
 
 // Workgroup -> (block, column tile) over the blocks that hold routed rows
 // (the first ntpp / block_m blocks; the rest of the capacity is tail).  The

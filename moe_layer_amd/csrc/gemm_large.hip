@@ -31,6 +31,8 @@
 //                  bf16 u) stored in expert-sorted order (P2 sections 1.1, 1.2).
 //   GEMM2 (a6):    tile = 256 output columns h; wave (wm, .) owns h0+64wm..;
 //                  epilogue y[f] = tw[f] * acc in fp32 (P2 section 1.1).
+//   The layer variants (router weight on the input, SwiGLU clamp) act in the
+//   epilogues as in the weight-streaming kernels.
 #include "common.h"
 
 namespace moe {
@@ -156,6 +158,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int row = blk * kBM + (2 * u + wn) * 32 + fr;
+            const float w_in = gemm1_row_weight(g, g.sorted_ids[row]);
 #pragma unroll
             for (int t = 0; t < kG; ++t) {
                 const int colw = tile * 128 + wm * (kTW / 2) + t * 32;
@@ -165,9 +168,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int i0 = q * 4 + 2 * h;
-                        const float a0 = silu_mul_bf16(round_bf16(acc[t][u][i0]), round_bf16(acc[t + kG][u][i0]));
+                        const float a0 =
+                            swiglu_bf16(acc[t][u][i0], acc[t + kG][u][i0], w_in, g.clamp, g.clamp_limit);
                         const float a1 =
-                            silu_mul_bf16(round_bf16(acc[t][u][i0 + 1]), round_bf16(acc[t + kG][u][i0 + 1]));
+                            swiglu_bf16(acc[t][u][i0 + 1], acc[t + kG][u][i0 + 1], w_in, g.clamp, g.clamp_limit);
                         p[h] = uint32_t(f32_to_bf16_rne(a0)) | (uint32_t(f32_to_bf16_rne(a1)) << 16);
                     }
                     const int col = colw + q * 8 + fk * 4;
@@ -181,7 +185,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
         for (int u = 0; u < NU; ++u) {
             const int f = g.sorted_ids[blk * kBM + (2 * u + wn) * 32 + fr];
             if (f >= R) continue;
-            const float tw = g.topk_weights[f];
+            const float tw = gemm2_row_weight(g, f);
             float* yrow = g.y + int64_t(f) * g.H;
 #pragma unroll
             for (int t = 0; t < kTA; ++t)

@@ -10,6 +10,10 @@
 // byte of K block g = [32g, 32g + 32) of row (l % 16).  So each K step of 128
 // is one instruction that applies both operands' block scales and accumulates
 // into the fp32 accumulator: no per-block rescaling on the vector ALUs.
+// GEMM2 runs on it.  GEMM1, whose results feed rounding decisions, runs on
+// the bf16 matrix cores instead: each lane dequantises its own MX block to
+// bf16 (exact for power-of-two scales), because the fp8 instruction's dot
+// product is not fp32-accurate (mx_compute).
 //
 // Orientation, tiles and epilogues follow the block-fp8 kernels: weights on
 // the MFMA M side (swap-AB, P1 section "Swap-AB"), the block's tokens on N,
@@ -17,7 +21,8 @@
 // rounding points (P2 section 1.2) and re-quantises the intermediate per row
 // and 32-column group (E8M0 scale + e4m3 codes, group amax exchanged through
 // LDS); GEMM2's multiplies by the router weight in fp32 and writes y by flat
-// slot.
+// slot.  The layer variants (router weight on the input, SwiGLU clamp) act in
+// the epilogues as in the block-fp8 kernels.
 #include "common.h"
 
 namespace moe {
@@ -31,9 +36,13 @@ constexpr int kTabStride = 4 * kTabSteps + 4;   // bytes per table row (padded b
 
 __device__ __forceinline__ i32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const i32x4*>(p); }
 
-// the lane's operand bytes of one K step: p points at K offset 16 * (l / 16)
+// The lane's operand bytes of one K step.  Scaled fp8 MFMA layout (kExact =
+// false): p points at K offset 16 * (l / 16), the second 16 bytes sit 64
+// further.  bf16 MFMA layout (kExact = true): p points at K offset
+// 32 * (l / 16), 32 contiguous bytes = the lane's MX block.
+template <bool kExact>
 __device__ __forceinline__ i32x8 ld32(const uint8_t* p) {
-    const i32x4 lo = ld16(p), hi = ld16(p + 64);
+    const i32x4 lo = ld16(p), hi = ld16(p + (kExact ? 16 : 64));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -63,53 +72,80 @@ struct MxAddr {
     const uint8_t* bs[NT];   // the lane's byte in the LDS token-scale table, step 0
 };
 
-template <int MT, int NT, int U>
+template <bool kExact, int MT, int NT, int U>
 __device__ __forceinline__ void mx_load(MxStage<MT, NT, U>& st, const MxAddr<MT, NT>& ad, int step0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t off = uint32_t(step0 + u) * kStepK;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            st.a[u][m] = ld32(ad.a[m] + (ad.aoff + off));
+            st.a[u][m] = ld32<kExact>(ad.a[m] + (ad.aoff + off));
             st.sa[u][m] = ad.as[m][ad.asoff + 4 * (step0 + u)];
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            st.b[u][n] = ld32(ad.b + (ad.boff[n] + off));
+            st.b[u][n] = ld32<kExact>(ad.b + (ad.boff[n] + off));
             st.sb[u][n] = ad.bs[n][4 * (step0 + u)];
         }
     }
 }
 
-template <int MT, int NT, int U>
+// One K step.  kExact = false: one scaled fp8 MFMA per tile pair.  kExact =
+// true: each lane dequantises its two MX blocks to bf16 (code * 2^(scale -
+// 127), exact) and four bf16 MFMAs accumulate the 128 products: the fp8
+// matrix-core dot product is not fp32-accurate on gfx950 (products smaller
+// than about 2^-14 of the largest in each group of eight are truncated,
+// measured), while the bf16 one is.  GEMM1 takes the exact form: its results
+// feed rounding decisions (the bf16 gate/up values and the intermediate's
+// e4m3 codes).
+template <bool kExact, int MT, int NT, int U>
 __device__ __forceinline__ void mx_compute(const MxStage<MT, NT, U>& st, f32x4 (&acc)[MT][NT]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+        if constexpr (kExact) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+            for (int q = 0; q < 4; ++q) {
+                bf16x8 bv[NT];
 #pragma unroll
-            for (int n = 0; n < NT; ++n)
-                acc[m][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    st.a[u][m], st.b[u][n], acc[m][n], 0, 0, 0, int(st.sa[u][m]), 0, int(st.sb[u][n]));
+                for (int n = 0; n < NT; ++n)
+                    bv[n] = e4m3x8_to_bf16(st.b[u][n][2 * q], st.b[u][n][2 * q + 1], e8m0_to_f32(st.sb[u][n]));
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const bf16x8 av =
+                        e4m3x8_to_bf16(st.a[u][m][2 * q], st.a[u][m][2 * q + 1], e8m0_to_f32(st.sa[u][m]));
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[n], acc[m][n], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        st.a[u][m], st.b[u][n], acc[m][n], 0, 0, 0, int(st.sa[u][m]), 0, int(st.sb[u][n]));
+        }
+    }
 }
 
 // K loop over nsteps steps, two register stages (the block-fp8 kernels' loop).
-template <int MT, int NT, int U>
+template <bool kExact, int MT, int NT, int U>
 __device__ __forceinline__ void mx_mainloop(const MxAddr<MT, NT>& ad, int nsteps, f32x4 (&acc)[MT][NT]) {
     MxStage<MT, NT, U> s0, s1;
-    mx_load<MT, NT, U>(s0, ad, 0);
+    mx_load<kExact, MT, NT, U>(s0, ad, 0);
     for (int k = 0; k < nsteps; k += 2 * U) {
         const bool has1 = k + U < nsteps;
-        if (has1) mx_load<MT, NT, U>(s1, ad, k + U);
-        mx_compute<MT, NT, U>(s0, acc);
-        if (k + 2 * U < nsteps) mx_load<MT, NT, U>(s0, ad, k + 2 * U);
-        if (has1) mx_compute<MT, NT, U>(s1, acc);
+        if (has1) mx_load<kExact, MT, NT, U>(s1, ad, k + U);
+        mx_compute<kExact, MT, NT, U>(s0, acc);
+        if (k + 2 * U < nsteps) mx_load<kExact, MT, NT, U>(s0, ad, k + 2 * U);
+        if (has1) mx_compute<kExact, MT, NT, U>(s1, acc);
     }
 }
 
 // Per chunk of kTabSteps K steps: stage the BM token rows' scale bytes
 // (row_scale(r) points at row r's first byte) in LDS, then run the K loop.
-template <int MT, int NT, int BM, int NTHREADS, typename RowScale>
+template <bool kExact, int MT, int NT, int BM, int NTHREADS, typename RowScale>
 __device__ __forceinline__ void mx_kloop(MxAddr<MT, NT> ad, RowScale row_scale, int nsteps, uint8_t* tab,
                                          f32x4 (&acc)[MT][NT]) {
     const int lane = threadIdx.x & 63;
@@ -134,7 +170,7 @@ __device__ __forceinline__ void mx_kloop(MxAddr<MT, NT> ad, RowScale row_scale, 
         ad.asoff = asoff0 + 4 * c0;
 #pragma unroll
         for (int n = 0; n < NT; ++n) ad.boff[n] = boff0[n] + uint32_t(c0) * kStepK;
-        mx_mainloop<MT, NT, 1>(ad, cs, acc);
+        mx_mainloop<kExact, MT, NT, 1>(ad, cs, acc);
     }
 }
 
@@ -170,7 +206,7 @@ __global__ __launch_bounds__(NW * 64) void gemm1_mx_kernel(GemmArgs g, int ntile
         ad.a[m] = w13 + row0 * H;
         ad.as[m] = w13s + row0 * kbh;
     }
-    ad.aoff = uint32_t(lr * H + lk * 16);
+    ad.aoff = uint32_t(lr * H + lk * 32);   // bf16 MFMA layout: the lane's MX block of the step
     ad.asoff = uint32_t(lr * kbh + lk);
     ad.b = g.xq;
     const int32_t* rows = g.sorted_ids + blk * BM;
@@ -178,7 +214,7 @@ __global__ __launch_bounds__(NW * 64) void gemm1_mx_kernel(GemmArgs g, int ntile
     for (int n = 0; n < NT; ++n) {
         const int f = rows[n * 16 + lr];
         const int tok = f < R ? f / g.topk : 0;   // padding rows read token 0, never stored as real rows
-        ad.boff[n] = uint32_t(tok) * uint32_t(H) + uint32_t(lk * 16);
+        ad.boff[n] = uint32_t(tok) * uint32_t(H) + uint32_t(lk * 32);
     }
 
     f32x4 acc[MT][NT];
@@ -192,17 +228,19 @@ __global__ __launch_bounds__(NW * 64) void gemm1_mx_kernel(GemmArgs g, int ntile
         const int f = rows[r];
         return xs + int64_t(f < R ? f / g.topk : 0) * kbh;
     };
-    mx_kloop<MT, NT, BM, NW * 64>(ad, row_scale, H / kStepK, tab, acc);
+    mx_kloop<true, MT, NT, BM, NW * 64>(ad, row_scale, H / kStepK, tab, acc);
 
     // epilogue: a = silu(g) * u with the bf16 rounding points
     float a[WT][NT][4];
 #pragma unroll
-    for (int m = 0; m < WT; ++m)
+    for (int n = 0; n < NT; ++n) {
+        const float w_in = gemm1_row_weight(g, g.sorted_ids[blk * BM + n * 16 + lr]);
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+        for (int m = 0; m < WT; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                a[m][n][j] = silu_mul_bf16(round_bf16(acc[m][n][j]), round_bf16(acc[WT + m][n][j]));
+                a[m][n][j] = swiglu_bf16(acc[m][n][j], acc[WT + m][n][j], w_in, g.clamp, g.clamp_limit);
+    }
 
     // per token, amax over each 32-column group: the wave's columns
     // i0 .. i0 + 16*WT - 1, lanes lk = 0..3 hold 4 columns each per tile
@@ -289,13 +327,13 @@ __global__ __launch_bounds__(NW * 64) void gemm2_mx_kernel(GemmArgs g, int ntile
     __shared__ __attribute__((aligned(16))) uint8_t tab[BM * kTabStride];
     const uint8_t* scales = reinterpret_cast<const uint8_t*>(g.inter_scale) + int64_t(blk) * BM * kbi;
     auto row_scale = [&](int r) { return scales + int64_t(r) * kbi; };
-    mx_kloop<MT, NT, BM, NW * 64>(ad, row_scale, I / kStepK, tab, acc);
+    mx_kloop<false, MT, NT, BM, NW * 64>(ad, row_scale, I / kStepK, tab, acc);
 
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const int f = g.sorted_ids[blk * BM + n * 16 + lr];
         if (f >= R) continue;
-        const float tw = g.topk_weights[f];
+        const float tw = gemm2_row_weight(g, f);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int col = h0 + m * 16 + 4 * lk;

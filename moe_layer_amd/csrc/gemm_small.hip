@@ -15,11 +15,16 @@
 //                  expert-sorted order (P2 section 1.1, sorted-A).
 //   GEMM2 (a6):    y = tw * (W2[e] . a), router weight applied in fp32 after the
 //                  GEMM (P2 section 1.1); rows scattered to y[f] by flat slot.
+//   Variants (P2 section 1.1 names both): with the router weight on the input
+//   the GEMM1 epilogue scales h by it and GEMM2 applies none; a SwiGLU clamp
+//   limit clamps the rounded gate/up pair (swiglu_bf16 in common.h).
 //
 // MFMA operand layouts (v_mfma_f32_16x16x32_bf16, v_mfma_f32_16x16x128_f8f6f4,
 // checked on gfx950): lane l holds row (l % 16) of A and column (l % 16) of B
 // at K offset (l / 16) * 8 elements (bf16) or (l / 16) * 32 (fp8); the 16x16
 // result gives lane l the column (l % 16), rows 4 * (l / 16) + 0..3.
+// fp8 GEMM1 multiplies on the bf16 matrix cores (operands dequantised in
+// registers, exactly; see compute_stage), fp8 GEMM2 on the fp8 ones.
 #include "common.h"
 
 namespace moe {
@@ -99,25 +104,83 @@ __device__ __forceinline__ void load_stage(Stage<FP8, MT, NT, U>& st, const uint
     }
 }
 
-template <bool FP8, int MT, int NT, int U>
+// One stage.  fp8: each 128-wide K block's partial product is scaled by
+// (weight block scale) * (activation group scale).  kExact (fp8 GEMM1): the
+// partial product comes from bf16 MFMAs on dequantised operands instead of one
+// fp8 MFMA: the lane's 32 bytes (K 32*(l/16) .. +31) become four 8-element
+// bf16 operands, the token's power-of-two group scale folded into its
+// operand exactly, and four 16x16x32 bf16 MFMAs sum the block.  The fp8
+// matrix-core dot product is not fp32-accurate on gfx950 (products below
+// about 2^-14 of the largest in each group of eight are truncated, measured)
+// while the bf16 one is, and GEMM1's results feed rounding decisions (the
+// bf16 gate/up values, the intermediate's e4m3 codes).
+template <bool FP8, bool kExact, int MT, int NT, int U>
 __device__ __forceinline__ void compute_stage(const Stage<FP8, MT, NT, U>& st, f32x4 (&acc)[MT][NT]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+        if constexpr (FP8 && kExact) {
+            f32x4 p[MT][NT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                if constexpr (FP8) {
-                    // one 128-wide K block: scale its partial product by
-                    // (weight block scale) * (activation group scale)
-                    const f32x4 p = mfma<FP8>(st.a[u][m], st.b[u][n], f32x4{0, 0, 0, 0});
-                    const float c = __fmul_rn(st.sa[u][m], st.sb[u][n]);
+                for (int n = 0; n < NT; ++n) p[m][n] = f32x4{0, 0, 0, 0};
+            // per 8-element chunk q: convert the smaller operand set once,
+            // stream the other (fewer live registers)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[m][n][j] = __builtin_fmaf(p[j], c, acc[m][n][j]);
+            for (int q = 0; q < 4; ++q) {
+                auto cvt_a = [&](int m) {
+                    return e4m3x8_to_bf16(st.a[u][m][q / 2][2 * (q % 2)], st.a[u][m][q / 2][2 * (q % 2) + 1], 1.0f);
+                };
+                auto cvt_b = [&](int n) {
+                    return e4m3x8_to_bf16(st.b[u][n][q / 2][2 * (q % 2)], st.b[u][n][q / 2][2 * (q % 2) + 1],
+                                          st.sb[u][n]);
+                };
+                if constexpr (NT <= MT) {
+                    bf16x8 bv[NT];
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) bv[n] = cvt_b(n);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        const bf16x8 av = cvt_a(m);
+#pragma unroll
+                        for (int n = 0; n < NT; ++n)
+                            p[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[n], p[m][n], 0, 0, 0);
+                    }
                 } else {
-                    acc[m][n] = mfma<FP8>(st.a[u][m], st.b[u][n], acc[m][n]);
+                    bf16x8 av[MT];
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) av[m] = cvt_a(m);
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        const bf16x8 bv = cvt_b(n);
+#pragma unroll
+                        for (int m = 0; m < MT; ++m)
+                            p[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv, p[m][n], 0, 0, 0);
+                    }
                 }
             }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[m][n][j] = __builtin_fmaf(p[m][n][j], st.sa[u][m], acc[m][n][j]);
+        } else {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    if constexpr (FP8) {
+                        const f32x4 p = mfma<FP8>(st.a[u][m], st.b[u][n], f32x4{0, 0, 0, 0});
+                        const float c = __fmul_rn(st.sa[u][m], st.sb[u][n]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[m][n][j] = __builtin_fmaf(p[j], c, acc[m][n][j]);
+                    } else {
+                        acc[m][n] = mfma<FP8>(st.a[u][m], st.b[u][n], acc[m][n]);
+                    }
+                }
+        }
+    }
 }
 
 // K loop over nsteps MFMA steps (nsteps % U == 0): load the next stage, then
@@ -126,7 +189,7 @@ __device__ __forceinline__ void compute_stage(const Stage<FP8, MT, NT, U>& st, f
 // and HBM latency is hidden by many waves per CU (the tiles are sized for
 // occupancy).  Deeper software pipelines (3-4 stages with scheduling
 // barriers) cost occupancy and measured slower on every decode shape.
-template <bool FP8, int MT, int NT, int U>
+template <bool FP8, bool kExact, int MT, int NT, int U>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&ap)[MT], const uint8_t* const (&bp)[NT],
                                          const float* const (&asp)[MT], const float* const (&bsp)[NT],
                                          int nsteps, f32x4 (&acc)[MT][NT]) {
@@ -135,16 +198,16 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&ap)[MT], const u
     for (int k = 0; k < nsteps; k += 2 * U) {
         const bool has1 = k + U < nsteps;
         if (has1) load_stage<FP8, MT, NT, U>(s1, ap, bp, asp, bsp, k + U);
-        compute_stage<FP8, MT, NT, U>(s0, acc);
+        compute_stage<FP8, kExact, MT, NT, U>(s0, acc);
         if (k + 2 * U < nsteps) load_stage<FP8, MT, NT, U>(s0, ap, bp, asp, bsp, k + 2 * U);
-        if (has1) compute_stage<FP8, MT, NT, U>(s1, acc);
+        if (has1) compute_stage<FP8, kExact, MT, NT, U>(s1, acc);
     }
 }
 
 // fp8 K loop: per chunk of kTabSteps K-blocks, stage the BM rows' activation
 // scales (row_scale(r) points at row r's first group) in LDS, then run the
 // mainloop over the chunk.  Every thread of the workgroup takes part.
-template <int MT, int NT, int BM, int NTHREADS, typename RowScale>
+template <bool kExact, int MT, int NT, int BM, int NTHREADS, typename RowScale>
 __device__ __forceinline__ void mainloop_fp8(const uint8_t* const (&ap)[MT], const uint8_t* const (&bp)[NT],
                                              const float* const (&asp)[MT], RowScale row_scale, int nsteps,
                                              float* tab, f32x4 (&acc)[MT][NT]) {
@@ -172,7 +235,7 @@ __device__ __forceinline__ void mainloop_fp8(const uint8_t* const (&ap)[MT], con
             bpc[n] = bp[n] + int64_t(c0) * O::kStepBytes;
             bspc[n] = tab + (n * 16 + lr) * kTabStride;
         }
-        mainloop<true, MT, NT, 1>(apc, bpc, aspc, bspc, cs, acc);
+        mainloop<true, kExact, MT, NT, 1>(apc, bpc, aspc, bspc, cs, acc);
     }
 }
 
@@ -232,20 +295,22 @@ __global__ __launch_bounds__(NW * 64) void gemm1_small_kernel(GemmArgs g, int nt
             const int f = rows[r];
             return g.xs + int64_t(f < R ? f / g.topk : 0) * kb_count;
         };
-        mainloop_fp8<MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, H / O::kStepK, tab, acc);
+        mainloop_fp8<true, MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, H / O::kStepK, tab, acc);
     } else {
-        mainloop<FP8, MT, NT, U>(ap, bp, asp, bsp, H / O::kStepK, acc);
+        mainloop<FP8, false, MT, NT, U>(ap, bp, asp, bsp, H / O::kStepK, acc);
     }
 
     // epilogue: a = silu(g) * u with the bf16 rounding points
     float a[WT][NT][4];
 #pragma unroll
-    for (int m = 0; m < WT; ++m)
+    for (int n = 0; n < NT; ++n) {
+        const float w_in = gemm1_row_weight(g, g.sorted_ids[blk * BM + n * 16 + lr]);
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+        for (int m = 0; m < WT; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                a[m][n][j] = silu_mul_bf16(round_bf16(acc[m][n][j]), round_bf16(acc[WT + m][n][j]));
+                a[m][n][j] = swiglu_bf16(acc[m][n][j], acc[WT + m][n][j], w_in, g.clamp, g.clamp_limit);
+    }
 
     if constexpr (!FP8) {
         uint16_t* out = static_cast<uint16_t*>(g.inter);
@@ -348,16 +413,16 @@ __global__ __launch_bounds__(NW * 64) void gemm2_small_kernel(GemmArgs g, int nt
         __shared__ float tab[BM * kTabStride];
         const float* scales = g.inter_scale + int64_t(blk) * BM * kb_count;
         auto row_scale = [&](int r) { return scales + int64_t(r) * kb_count; };
-        mainloop_fp8<MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, I / O::kStepK, tab, acc);
+        mainloop_fp8<false, MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, I / O::kStepK, tab, acc);
     } else {
-        mainloop<FP8, MT, NT, U>(ap, bp, asp, bsp, I / O::kStepK, acc);
+        mainloop<FP8, false, MT, NT, U>(ap, bp, asp, bsp, I / O::kStepK, acc);
     }
 
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const int f = g.sorted_ids[blk * BM + n * 16 + lr];
         if (f >= R) continue;
-        const float tw = g.topk_weights[f];
+        const float tw = gemm2_row_weight(g, f);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int col = h0 + m * 16 + 4 * lk;

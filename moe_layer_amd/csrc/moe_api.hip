@@ -14,7 +14,7 @@ using namespace moe;
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 1;   // 1.1: MXFP8 weights
+constexpr int kVersionMinor = 2;   // 1.1: MXFP8 weights; 1.2: layer variants (flags, clamp_limit)
 // rows per expert from which the LDS-tiled path beats weight streaming
 constexpr double kLargeMinRowsPerExpert = 96.0;
 // From this many routed slots on, the alignment runs on many workgroups (one
@@ -42,6 +42,8 @@ int validate_forward_scalars(const moe_forward_args* a) {
     if (a->wdtype != MOE_WDTYPE_BF16 && a->wdtype != MOE_WDTYPE_FP8_E4M3 && a->wdtype != MOE_WDTYPE_MXFP8)
         return MOE_ERR_INVALID_ARG;
     if (a->path < MOE_PATH_AUTO || a->path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
+    if ((a->flags & ~MOE_FLAG_WEIGHT_ON_INPUT) != 0) return MOE_ERR_INVALID_ARG;
+    if (!(a->clamp_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;   // negative or NaN
     if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 256)
         return MOE_ERR_UNSUPPORTED;
     const int q = a->wdtype == MOE_WDTYPE_BF16 ? 64 : MOE_QUANT_GROUP;
@@ -249,6 +251,9 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
     g.inter = ws + p.off_inter;
     g.inter_scale = fp8 ? reinterpret_cast<float*>(ws + p.off_inter_scale) : nullptr;
     g.y = reinterpret_cast<float*>(ws + p.off_y);
+    g.weight_on_input = (a->flags & MOE_FLAG_WEIGHT_ON_INPUT) != 0;
+    g.clamp = a->clamp_limit > 0.0f;
+    g.clamp_limit = a->clamp_limit;
 
     auto mark = [&](int i) { return ev ? hip_status(hipEventRecord(ev[i], stream)) : MOE_OK; };
     if ((st = mark(0)) != MOE_OK) return st;

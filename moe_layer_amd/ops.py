@@ -19,6 +19,7 @@ _lib = None
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_WDTYPE_BF16, MOE_WDTYPE_FP8_E4M3, MOE_WDTYPE_MXFP8 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_SMALL_M, MOE_PATH_LARGE_M = 0, 1, 2
+MOE_FLAG_WEIGHT_ON_INPUT = 1
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_QUANT_GROUP, MOE_MX_BLOCK = 1024, 64, 128, 32
 
 # every entry point include/moe.h declares
@@ -41,7 +42,8 @@ class ForwardArgs(C.Structure):
                 ("x", C.c_void_p), ("w13", C.c_void_p), ("w13_scale", C.c_void_p),
                 ("w2", C.c_void_p), ("w2_scale", C.c_void_p),
                 ("topk_ids", C.c_void_p), ("topk_weights", C.c_void_p), ("out", C.c_void_p),
-                ("path", C.c_int32), ("block_m", C.c_int32)]
+                ("path", C.c_int32), ("block_m", C.c_int32),
+                ("flags", C.c_int32), ("clamp_limit", C.c_float)]
 
 
 class PlanInfo(C.Structure):
@@ -174,9 +176,11 @@ def _u8(t):
 
 
 def forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=None, out=None,
-                 path=MOE_PATH_AUTO, block_m=0, shape=None) -> ForwardArgs:
+                 path=MOE_PATH_AUTO, block_m=0, shape=None, weight_on_input=False,
+                 clamp_limit=0.0) -> ForwardArgs:
     """Build the moe_forward_args struct.  With ``shape=(T, E, H, I, topk, wdtype)``
-    the tensors may be None (for planning and validation)."""
+    the tensors may be None (for planning and validation).  ``weight_on_input``
+    and ``clamp_limit`` select the layer variants (0: no clamp)."""
     if shape is None:
         T, H = x.shape
         E, twoI, _ = w13.shape
@@ -193,6 +197,8 @@ def forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=No
     a.w2, a.w2_scale = _ptr(_u8(w2)), _ptr(w2_scale)
     a.topk_ids, a.topk_weights, a.out = _ptr(topk_ids), _ptr(topk_weights), _ptr(out)
     a.path, a.block_m = path, block_m
+    a.flags = MOE_FLAG_WEIGHT_ON_INPUT if weight_on_input else 0
+    a.clamp_limit = clamp_limit
     return a
 
 
@@ -210,15 +216,18 @@ def moe_forward_workspace(args: ForwardArgs) -> int:
 
 
 def moe_forward(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=None, out=None,
-                workspace=None, path=MOE_PATH_AUTO, block_m=0):
+                workspace=None, path=MOE_PATH_AUTO, block_m=0, weight_on_input=False, clamp_limit=0.0):
     """The fused MoE layer: bf16 x [T,H], w13 [E,2I,H], w2 [E,H,I] (bf16; or
     e4m3 with fp32 128x128 block scales; or e4m3 with E8M0 uint8 scales per row
     and 32 K elements, MXFP8), int32 ids [T,k], fp32 weights [T,k].
+    ``weight_on_input``: the router weight scales GEMM1's input row instead of
+    GEMM2's output; ``clamp_limit`` > 0: SwiGLU clamp (gate <= L, |up| <= L).
     Returns (out bf16 [T,H], workspace)."""
     T, H = x.shape
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out, path, block_m)
+    a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out, path, block_m,
+                     weight_on_input=weight_on_input, clamp_limit=clamp_limit)
     need = moe_forward_workspace(a)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)

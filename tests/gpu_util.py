@@ -123,8 +123,10 @@ def routing(cfg: Config):
     return ids, w, lg
 
 
-def oracle_tokens(layer: DeviceLayer, x64: np.ndarray, ids: np.ndarray, tw: np.ndarray, tokens) -> np.ndarray:
-    """Unrounded oracle output rows for the given tokens, one expert at a time."""
+def oracle_tokens(layer: DeviceLayer, x64: np.ndarray, ids: np.ndarray, tw: np.ndarray, tokens,
+                  weight_on_input: bool = False, clamp_limit: float = 0.0) -> np.ndarray:
+    """Unrounded oracle output rows for the given tokens, one expert at a time
+    (with the layer variants as moe_forward takes them: clamp_limit 0 = none)."""
     tokens = np.asarray(tokens)
     fp8 = layer.cfg.wdtype != "bf16"
     group = 32 if layer.cfg.wdtype == "mxfp8" else 128
@@ -139,7 +141,8 @@ def oracle_tokens(layer: DeviceLayer, x64: np.ndarray, ids: np.ndarray, tw: np.n
         w13, w2 = layer.exact(e)
         rows_i = [i for i, _ in lst]
         y = O.expert_rows(x64, w13, w2, tokens[rows_i], [tw[tokens[i], j] for i, j in lst], fp8=fp8,
-                          group=group)
+                          group=group, weight_on_input=weight_on_input,
+                          clamp_limit=float(clamp_limit) if clamp_limit > 0 else None)
         np.add.at(out, rows_i, y)
     return out
 

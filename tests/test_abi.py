@@ -59,8 +59,11 @@ def test_align_capacity_errors():
     assert L.moe_align_capacity(2 ** 28, 64, 1024, 1024) == ops.MOE_ERR_UNSUPPORTED
 
 
-def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAKE, scales=True):
-    a = ops.forward_args(None, None, None, None, None, shape=(T, E, H, I, k, wdtype), path=path, block_m=block_m)
+def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAKE, scales=True, flags=0,
+          clamp_limit=0.0):
+    a = ops.forward_args(None, None, None, None, None, shape=(T, E, H, I, k, wdtype), path=path, block_m=block_m,
+                         clamp_limit=clamp_limit)
+    a.flags = flags
     for f in ("x", "w13", "w2", "topk_ids", "topk_weights", "out"):
         setattr(a, f, ptr)
     if wdtype in (ops.MOE_WDTYPE_FP8_E4M3, ops.MOE_WDTYPE_MXFP8) and scales:
@@ -145,10 +148,25 @@ def test_plan_large_path_limits():
     (dict(H=4032, wdtype=2, I=256), ops.MOE_ERR_UNSUPPORTED),   # MXFP8 needs H % 128 == 0
     (dict(wdtype=3), ops.MOE_ERR_INVALID_ARG),
     (dict(T=1 << 20, H=4096, I=256, wdtype=2), ops.MOE_ERR_UNSUPPORTED),   # MXFP8: T * H < 2^32
+    (dict(flags=2), ops.MOE_ERR_INVALID_ARG),               # unknown flag bit
+    (dict(flags=-1), ops.MOE_ERR_INVALID_ARG),
+    (dict(clamp_limit=-1.0), ops.MOE_ERR_INVALID_ARG),
+    (dict(clamp_limit=float("nan")), ops.MOE_ERR_INVALID_ARG),
+    (dict(clamp_limit=-0.0, ptr=None), ops.MOE_ERR_INVALID_ARG),   # -0 is "no clamp": the null pointer decides
 ])
 def test_forward_validation(kw, status):
     a = _args(**kw)
     assert ops.lib().moe_forward(C.byref(a), C.c_void_p(FAKE), 1 << 40, None) == status
+
+
+def test_forward_variants_plan_like_the_plain_layer():
+    """The variants change only the epilogues: same plan, same workspace."""
+    base = ops.moe_plan(_args())
+    for kw in (dict(flags=ops.MOE_FLAG_WEIGHT_ON_INPUT), dict(clamp_limit=7.0), dict(clamp_limit=float("inf")),
+               dict(flags=ops.MOE_FLAG_WEIGHT_ON_INPUT, clamp_limit=0.5, wdtype=1, I=256)):
+        p = ops.moe_plan(_args(**kw))
+        ref = base if "wdtype" not in kw else ops.moe_plan(_args(wdtype=1, I=256))
+        assert p == ref
 
 
 def test_forward_workspace_errors():

@@ -167,7 +167,8 @@ def _forward_case(cfg, tokens=None, **kw):
     out, ws, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw32, **kw)
     gpu = out.to(torch.float64).cpu().numpy()
     tokens = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
-    o = oracle_tokens(layer, wl.x_exact(), ids_o, tw_o, tokens)
+    o = oracle_tokens(layer, wl.x_exact(), ids_o, tw_o, tokens, kw.get("weight_on_input", False),
+                      kw.get("clamp_limit", 0.0))
     excess, raw, floor = compare_output(gpu[tokens], o)
     log(f"  excess/RMS={excess:.3e} raw max/RMS={raw:.3e} bf16 floor/RMS={floor:.3e}")
     assert np.all(np.isfinite(gpu))
@@ -368,3 +369,61 @@ def test_plan_reports_the_path_taken():
     a = ops.forward_args(None, None, None, None, None, shape=(cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk, 0))
     p = ops.moe_plan(a)
     assert p["path"] == ops.MOE_PATH_SMALL_M and p["block_m"] == 16
+
+
+# ------------------------------------------------------------ layer variants ---
+
+# A clamp limit that is not a bf16 value (the clamp acts after the bf16
+# rounding of gate/up) and that the tiny layer's gate/up values often exceed.
+_LIMIT = float(np.float32(0.07))
+_VARIANTS = {"on_input": dict(weight_on_input=True), "clamp": dict(clamp_limit=_LIMIT),
+             "both": dict(weight_on_input=True, clamp_limit=_LIMIT)}
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("variant", sorted(_VARIANTS))
+@pytest.mark.parametrize("block_m", [16, 64])
+def test_forward_variants_tiny(wdtype, variant, block_m):
+    _forward_case(replace(CONFIGS["tiny"], wdtype=wdtype), block_m=block_m, **_VARIANTS[variant])
+
+
+@pytest.mark.parametrize("variant", sorted(_VARIANTS))
+def test_forward_variants_large_path(variant):
+    _forward_case(CONFIGS["tiny"], path=ops.MOE_PATH_LARGE_M, **_VARIANTS[variant])
+
+
+@pytest.mark.parametrize("name,variant", [("decode", "both"), ("fp8", "clamp"), ("mxfp8", "clamp")])
+def test_forward_variants_workloads(name, variant):
+    _forward_case(CONFIGS[name], **_VARIANTS[variant])
+
+
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("variant", ["on_input", "both"])
+def test_forward_weight_on_input_top1_workload(wdtype, variant):
+    """The router weight on the input at the fp8 layer's shape with top-1
+    routing (one slot per token carries the weight) and weights spread over
+    [0.1, 1)."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config(f"{wdtype}_top1", 1024, 256, 4096, 256, 1, wdtype, "given")
+    wl = Workload(cfg)
+    ids, _ = wl.given_routing()
+    tw = np.random.default_rng(17).uniform(0.1, 1.0, size=(cfg.T, 1)).astype(np.float32)
+    layer = layer_for(cfg)
+    layer.ensure(np.unique(ids))
+    kw = _VARIANTS[variant]
+    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, **kw)
+    gpu = out.to(torch.float64).cpu().numpy()
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(cfg.T),
+                      kw.get("weight_on_input", False), kw.get("clamp_limit", 0.0))
+    excess, raw, _ = compare_output(gpu, o)
+    log(f"{wdtype} top-1 {variant}: excess/RMS={excess:.3e} raw={raw:.3e}")
+    assert excess <= TAU[wdtype]
+
+
+def test_forward_variants_change_the_output():
+    """The variants are live on the GPU: each moves the tiny layer's output."""
+    cfg = replace(CONFIGS["tiny"], wdtype="bf16")
+    base, _ = _forward_case(cfg)
+    for v in ("on_input", "clamp"):
+        out, _ = _forward_case(cfg, **_VARIANTS[v])
+        assert not torch.equal(out, base), v
