@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--path", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-layer", action="store_true",
+                    help="run each step as one moe_decode_layer launch (routing inside the kernel)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region run one plain 1 GiB device copy (HBM counter calibration)")
@@ -62,8 +64,9 @@ def parse():
 
 # sources each dominant kernel is built from (its HBM traffic counters are
 # valid only while these are unchanged)
-KERNEL_SOURCES = {"small": ("gemm_small.hip", "common.h"), "large": ("gemm_large.hip", "common.h"),
-                  "mx": ("gemm_mx.hip", "common.h")}
+KERNEL_SOURCES = {"small": ("gemm_small.hip", "dev_gemm_small.h", "common.h"),
+                  "large": ("gemm_large.hip", "common.h"),
+                  "mx": ("gemm_mx.hip", "dev_gemm_mx.h", "common.h")}
 
 
 def kernel_source_digest(path: str) -> str:
@@ -171,7 +174,20 @@ def main():
     lib = ops.lib()
     import ctypes as C
 
+    use_dl = args.decode_layer
+    if use_dl and not plan["decode_layer"]:
+        raise SystemExit("--decode-layer: moe_decode_layer does not take this workload (moe_plan)")
+    sync = torch.zeros(ops.MOE_SYNC_WORDS, dtype=torch.int32, device=d)
+
     def step():
+        if use_dl:
+            st = lib.moe_decode_layer(C.byref(fargs), C.c_void_p(logits.data_ptr()) if logits is not None else None,
+                                      1, C.c_void_p(ids.data_ptr()), C.c_void_p(tw.data_ptr()),
+                                      C.c_void_p(sync.data_ptr()), C.c_void_p(ws.data_ptr()), ws.numel(),
+                                      C.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError(ops.status_string(st))
+            return
         if logits is not None:
             ops.moe_route(logits, k, True, ids, tw)
         st = lib.moe_forward(C.byref(fargs), C.c_void_p(ws.data_ptr()), ws.numel(),
@@ -252,6 +268,17 @@ def main():
     roof["algorithmic_flops"] = g1_flops
     roof["hbm_frac"] = round(g1_gbs / HBM_PEAK_GBS, 4)
     roof["mfma_frac"] = round(g1_tfs / peak_tf, 4)
+    if use_dl:
+        # one launch per step: the dominant kernel is the whole layer
+        if int(sync.abs().sum()) != 0:
+            raise RuntimeError(f"decode layer barrier buffer not clean: {sync.cpu().numpy()}")
+        l_gbs = layer_bytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(l_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(l_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_layer_kernel (route, align, GEMM1 + SiLU-mul, GEMM2, combine in one launch)",
+                "kernel_ms": round(float(ms), 5), "algorithmic_bytes": int(layer_bytes),
+                "algorithmic_flops": layer_flops, "hbm_frac": round(l_gbs / HBM_PEAK_GBS, 4),
+                "mfma_frac": None}
 
     mfma_floor_s = g1_flops / (GEMM1_PEAK_TFLOPS * 1e12) + (layer_flops - g1_flops) / (
         GEMM2_PEAK_TFLOPS[cfg.wdtype] * 1e12)
@@ -269,6 +296,7 @@ def main():
                    "T": T, "E": E, "H": H, "I": I, "topk": k, "weights": cfg.wdtype,
                    "block_m": plan["block_m"], "path": ["auto", "small_m", "large_m"][plan["path"]],
                    "gemm1_mfma": "bf16", "gemm2_mfma": cfg.wdtype,
+                   "launch": "one decode-layer kernel" if use_dl else "one kernel per stage",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

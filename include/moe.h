@@ -202,7 +202,7 @@ typedef struct moe_plan_info {
     int32_t num_blocks;    /* ceil(capacity / block_m): GEMM grid rows */
     int32_t gemm1_cols;    /* GEMM1 weight rows (of 2I, gate + up) per workgroup */
     int32_t gemm2_cols;    /* GEMM2 weight rows (of H) per workgroup */
-    int32_t reserved;
+    int32_t decode_layer;  /* 1 if moe_decode_layer takes these arguments */
     int64_t workspace_bytes;
     /* byte offsets of the forward's intermediates inside the workspace */
     int64_t off_sorted_ids, off_expert_ids, off_num_post_padded;
@@ -270,6 +270,42 @@ MOE_API int moe_forward(const moe_forward_args* a, void* workspace, int64_t work
 #define MOE_NUM_STAGES 5
 MOE_API int moe_forward_profiled(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
                                  hipStream_t stream, hipEvent_t* events, int32_t n_events);
+
+/*
+ * moe_decode_layer — the whole layer for few tokens (decode) in ONE kernel
+ * launch: [router top-k from logits] and [fp8 activation quantisation] ->
+ * alignment -> GEMM1 + SiLU-mul epilogue -> GEMM2 -> top-k combine, the phases
+ * separated by grid-wide barriers inside a persistent cooperative kernel
+ * (P3, section on MoE dispatch/combine: the decode-side kernels are fused
+ * into one, since per-kernel latency is a visible share at a few tokens per
+ * step).  Results are bitwise those of moe_route + moe_forward.
+ *
+ *   a                  as for moe_forward (layer variants included);
+ *   router_logits      device fp32 [T, E], or NULL.  With logits the layer
+ *                      routes them as moe_route(renormalize) does and writes
+ *                      the routing to topk_ids_out / topk_weights_out (device
+ *                      int32 / fp32 [T, topk]; a->topk_ids and
+ *                      a->topk_weights are not read).  With NULL, the routing
+ *                      is a->topk_ids / a->topk_weights and the outputs are
+ *                      not written.
+ *   sync               device uint32 [MOE_SYNC_WORDS], all zero before the
+ *                      first call; every call leaves it zero.  Calls sharing a
+ *                      sync buffer must be ordered on one stream.  If a
+ *                      grid-barrier wait ever exceeds 2 s (the device could
+ *                      not keep every workgroup resident), the kernel sets
+ *                      sync[MOE_SYNC_ERROR] and finishes with an undefined
+ *                      output; the buffer must then be zeroed again.
+ *   workspace          as for moe_forward (same size and layout).
+ * Supported where moe_plan reports decode_layer = 1: the weight-streaming
+ * path with block_m 16, T * topk <= 256, H % 256 == 0, I % 128 == 0 (else
+ * MOE_ERR_UNSUPPORTED); with logits also topk <= E.  The device must support
+ * cooperative launches (else MOE_ERR_HIP).
+ */
+#define MOE_SYNC_WORDS 640   /* 2560 bytes */
+#define MOE_SYNC_ERROR 576
+MOE_API int moe_decode_layer(const moe_forward_args* a, const float* router_logits, int32_t renormalize,
+                             int32_t* topk_ids_out, float* topk_weights_out, uint32_t* sync, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@
 //                        tail and block experts; many workgroups scatter.
 //                        Used when the slot count is large enough that one
 //                        CU's ALUs would be the bottleneck.
-#include "common.h"
+#include "dev_align.h"
 
 namespace moe {
 
@@ -27,18 +27,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxE = 1024;
 constexpr int kBatchUnroll = 4;   // batches whose loads are issued together
 
-__device__ __forceinline__ uint64_t peers(int e, bool valid, int nbits) {
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t bb = __ballot(valid && bit);
-        m &= bit ? bb : ~bb;
-    }
-    return valid ? m : 0ull;
-}
 
 __global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restrict__ ids, int R,
                                                         int E, int B, int cap,
@@ -174,82 +164,14 @@ __global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restri
 // ---------------------------------------------------------------------------
 // one-wave form for few slots (decode): no cross-wave synchronisation
 // ---------------------------------------------------------------------------
-constexpr int kTinyBatches = 4;
-constexpr int kTinyMaxSlots = 64 * kTinyBatches;
-
 __global__ __launch_bounds__(64) void align_tiny_kernel(const int32_t* __restrict__ ids, int R, int E, int B,
                                                        int cap, int32_t* __restrict__ sorted,
                                                        int32_t* __restrict__ expert_ids,
                                                        int32_t* __restrict__ ntpp,
                                                        int32_t* __restrict__ inv) {
-    __shared__ int cnt[kMaxE];    // counts, then running positions
+    __shared__ int cnt[kMaxE];
     __shared__ int offs[kMaxE + 1];
-    const int lane = threadIdx.x;
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
-    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    int ev[kTinyBatches];
-#pragma unroll
-    for (int u = 0; u < kTinyBatches; ++u) {
-        const int f = 64 * u + lane;
-        ev[u] = f < R ? ids[f] : -1;
-    }
-    for (int e = lane; e < E; e += 64) cnt[e] = 0;
-    __syncthreads();
-    uint64_t m[kTinyBatches];
-#pragma unroll
-    for (int u = 0; u < kTinyBatches; ++u) {
-        const int e = ev[u];
-        const bool valid = e >= 0 && e < E;
-        m[u] = peers(e, valid, nbits);
-        if (valid && (m[u] & lt_mask) == 0) cnt[e] += __popcll(m[u]);
-        __syncthreads();   // batches of one expert update its count in order
-    }
-    // lane owns experts [lane * per, lane * per + per): padded sizes, scan
-    const int per = (E + 63) / 64;
-    const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
-    int mine = 0;
-    for (int e = e0; e < e1; ++e) mine += (cnt[e] + B - 1) / B * B;
-    int incl = mine;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
-    int run = incl - mine;
-    for (int e = e0; e < e1; ++e) {
-        const int c = cnt[e];
-        const int padded = (c + B - 1) / B * B;
-        offs[e] = run;
-        for (int p = run + c; p < run + padded; ++p) sorted[p] = R;            // padding
-        for (int b = run / B; b < (run + padded) / B; ++b) expert_ids[b] = e;  // its blocks
-        cnt[e] = run;
-        run += padded;
-    }
-    const int total = __shfl(incl, 63);
-    if (lane == 0) {
-        offs[E] = total;
-        ntpp[0] = total;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kTinyBatches; ++u) {
-        const int f = 64 * u + lane;
-        const int e = ev[u];
-        const bool valid = e >= 0 && e < E;
-        if (valid) {
-            const int pos = cnt[e] + __popcll(m[u] & lt_mask);
-            sorted[pos] = f;
-            if (inv) inv[f] = pos;
-        } else if (f < R && inv) {
-            inv[f] = -1;
-        }
-        __syncthreads();
-        if (valid && (m[u] & lt_mask) == 0) cnt[e] += __popcll(m[u]);
-        __syncthreads();
-    }
-    for (int p = total + lane; p < cap; p += 64) sorted[p] = R;
-    const int nblocks = (cap + B - 1) / B;
-    for (int b = total / B + lane; b < nblocks; b += 64) expert_ids[b] = -1;
+    align_tiny_wg(ids, R, E, B, cap, sorted, expert_ids, ntpp, inv, cnt, offs, true);
 }
 
 // ---------------------------------------------------------------------------

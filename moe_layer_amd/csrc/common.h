@@ -235,6 +235,13 @@ hipError_t launch_gemm2_large(const GemmArgs& g, bool fp8, hipStream_t s);
 bool gemm_large_supported(int H, int I, bool fp8);   // shapes the LDS-tiled path handles
 int gemm_large_block_m();                            // its rows per expert block
 
+// The single-launch decode layer (fused.hip): block_m 16 and the shapes below.
+bool decode_layer_supported(int T, int topk, int H, int I, int block_m);
+hipError_t launch_decode_layer(const GemmArgs& g, int wdtype_fp8, int mx, const float* logits, int renormalize,
+                               int32_t* route_ids, float* route_weights, const int32_t* ids, int32_t* sorted,
+                               int32_t* expert_ids, int32_t* ntpp, int cap, uint8_t* xq, void* xs, uint16_t* out,
+                               uint32_t* sync, hipStream_t s);
+
 hipError_t launch_combine(const float* y, const int32_t* ids, int T, int topk, int E, int H,
                           uint16_t* out, hipStream_t s);
 

@@ -14,7 +14,7 @@ using namespace moe;
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 2;   // 1.1: MXFP8 weights; 1.2: layer variants (flags, clamp_limit)
+constexpr int kVersionMinor = 3;   // 1.1: MXFP8 weights; 1.2: layer variants; 1.3: moe_decode_layer
 // rows per expert from which the LDS-tiled path beats weight streaming
 constexpr double kLargeMinRowsPerExpert = 96.0;
 // From this many routed slots on, the alignment runs on many workgroups (one
@@ -108,6 +108,37 @@ int make_plan(const moe_forward_args* a, Plan* p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The GEMM kernels' arguments for a validated plan and workspace.
+GemmArgs gemm_args(const moe_forward_args* a, const Plan& p, uint8_t* ws) {
+    const bool fp8 = a->wdtype != MOE_WDTYPE_BF16;
+    GemmArgs g{};
+    g.T = a->T;
+    g.E = a->E;
+    g.H = a->H;
+    g.I = a->I;
+    g.topk = a->topk;
+    g.block_m = p.block_m;
+    g.num_blocks = p.num_blocks;
+    g.x = static_cast<const uint16_t*>(a->x);
+    g.xq = fp8 ? ws + p.off_xq : nullptr;
+    g.xs = fp8 ? reinterpret_cast<const float*>(ws + p.off_xs) : nullptr;
+    g.w13 = a->w13;
+    g.w13_scale = a->w13_scale;
+    g.w2 = a->w2;
+    g.w2_scale = a->w2_scale;
+    g.topk_weights = a->topk_weights;
+    g.sorted_ids = reinterpret_cast<const int32_t*>(ws + p.off_sorted);
+    g.expert_ids = reinterpret_cast<const int32_t*>(ws + p.off_eids);
+    g.ntpp = reinterpret_cast<const int32_t*>(ws + p.off_ntpp);
+    g.inter = ws + p.off_inter;
+    g.inter_scale = fp8 ? reinterpret_cast<float*>(ws + p.off_inter_scale) : nullptr;
+    g.y = reinterpret_cast<float*>(ws + p.off_y);
+    g.weight_on_input = (a->flags & MOE_FLAG_WEIGHT_ON_INPUT) != 0;
+    g.clamp = a->clamp_limit > 0.0f;
+    g.clamp_limit = a->clamp_limit;
+    return g;
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,7 +220,7 @@ MOE_API int moe_plan(const moe_forward_args* a, moe_plan_info* out) {
     out->num_blocks = p.num_blocks;
     out->gemm1_cols = p.gemm1_cols;
     out->gemm2_cols = p.gemm2_cols;
-    out->reserved = 0;
+    out->decode_layer = p.path == MOE_PATH_SMALL_M && decode_layer_supported(a->T, a->topk, a->H, a->I, p.block_m);
     out->workspace_bytes = p.total;
     out->off_sorted_ids = p.off_sorted;
     out->off_expert_ids = p.off_eids;
@@ -229,32 +260,7 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    GemmArgs g{};
-    g.T = a->T;
-    g.E = a->E;
-    g.H = a->H;
-    g.I = a->I;
-    g.topk = a->topk;
-    g.block_m = p.block_m;
-    g.num_blocks = p.num_blocks;
-    g.x = static_cast<const uint16_t*>(a->x);
-    g.xq = fp8 ? ws + p.off_xq : nullptr;
-    g.xs = fp8 ? reinterpret_cast<const float*>(ws + p.off_xs) : nullptr;
-    g.w13 = a->w13;
-    g.w13_scale = a->w13_scale;
-    g.w2 = a->w2;
-    g.w2_scale = a->w2_scale;
-    g.topk_weights = a->topk_weights;
-    g.sorted_ids = reinterpret_cast<const int32_t*>(ws + p.off_sorted);
-    g.expert_ids = reinterpret_cast<const int32_t*>(ws + p.off_eids);
-    g.ntpp = reinterpret_cast<const int32_t*>(ws + p.off_ntpp);
-    g.inter = ws + p.off_inter;
-    g.inter_scale = fp8 ? reinterpret_cast<float*>(ws + p.off_inter_scale) : nullptr;
-    g.y = reinterpret_cast<float*>(ws + p.off_y);
-    g.weight_on_input = (a->flags & MOE_FLAG_WEIGHT_ON_INPUT) != 0;
-    g.clamp = a->clamp_limit > 0.0f;
-    g.clamp_limit = a->clamp_limit;
-
+    GemmArgs g = gemm_args(a, p, ws);
     auto mark = [&](int i) { return ev ? hip_status(hipEventRecord(ev[i], stream)) : MOE_OK; };
     if ((st = mark(0)) != MOE_OK) return st;
     int32_t* sorted = reinterpret_cast<int32_t*>(ws + p.off_sorted);
@@ -304,6 +310,42 @@ MOE_API int moe_forward_profiled(const moe_forward_args* a, void* workspace, int
                                  hipStream_t stream, hipEvent_t* events, int32_t n_events) {
     if (!events || n_events < MOE_NUM_STAGES + 1) return MOE_ERR_INVALID_ARG;
     return run_forward(a, workspace, workspace_bytes, stream, events);
+}
+
+MOE_API int moe_decode_layer(const moe_forward_args* a, const float* router_logits, int32_t renormalize,
+                             int32_t* topk_ids_out, float* topk_weights_out, uint32_t* sync, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream) {
+    Plan p;
+    int st = make_plan(a, &p);
+    if (st != MOE_OK) return st;
+    if (p.path != MOE_PATH_SMALL_M || !decode_layer_supported(a->T, a->topk, a->H, a->I, p.block_m))
+        return MOE_ERR_UNSUPPORTED;
+    if (a->T == 0) return MOE_OK;
+    const bool fp8 = a->wdtype != MOE_WDTYPE_BF16;
+    const bool mx = a->wdtype == MOE_WDTYPE_MXFP8;
+    if (router_logits) {
+        if (a->topk > a->E || !aligned(router_logits, 4) || !topk_ids_out || !topk_weights_out ||
+            !aligned(topk_ids_out, 4) || !aligned(topk_weights_out, 4))
+            return MOE_ERR_INVALID_ARG;
+    } else if (!a->topk_ids || !a->topk_weights || !aligned(a->topk_ids, 4) || !aligned(a->topk_weights, 4)) {
+        return MOE_ERR_INVALID_ARG;
+    }
+    if (!a->x || !a->w13 || !a->w2 || !a->out || !aligned(a->x, 16) || !aligned(a->w13, 16) ||
+        !aligned(a->w2, 16) || !aligned(a->out, 16) || !sync || !aligned(sync, 4))
+        return MOE_ERR_INVALID_ARG;
+    if (fp8 && (!a->w13_scale || !a->w2_scale || !aligned(a->w13_scale, 4) || !aligned(a->w2_scale, 4)))
+        return MOE_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    GemmArgs g = gemm_args(a, p, ws);
+    const int32_t* ids = router_logits ? topk_ids_out : a->topk_ids;
+    if (router_logits) g.topk_weights = topk_weights_out;
+    return hip_status(launch_decode_layer(
+        g, fp8, mx, router_logits, renormalize, topk_ids_out, topk_weights_out, ids,
+        reinterpret_cast<int32_t*>(ws + p.off_sorted), reinterpret_cast<int32_t*>(ws + p.off_eids),
+        reinterpret_cast<int32_t*>(ws + p.off_ntpp), int(p.cap), fp8 ? ws + p.off_xq : nullptr,
+        fp8 ? static_cast<void*>(ws + p.off_xs) : nullptr, static_cast<uint16_t*>(a->out), sync, stream));
 }
 
 }  // extern "C"

@@ -25,8 +25,9 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_QUANT_GROUP, MOE_MX_BLOCK = 1024, 64, 128, 32
 # every entry point include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_version", "moe_route", "moe_align_capacity", "moe_align",
            "moe_quant_act", "moe_quant_act_mx", "moe_plan", "moe_forward_workspace", "moe_forward",
-           "moe_forward_profiled")
+           "moe_forward_profiled", "moe_decode_layer")
 MOE_NUM_STAGES = 5
+MOE_SYNC_WORDS, MOE_SYNC_ERROR = 640, 576
 STAGE_NAMES = ("align", "quant_act", "gemm1", "gemm2", "combine")
 
 
@@ -49,7 +50,7 @@ class ForwardArgs(C.Structure):
 class PlanInfo(C.Structure):
     _fields_ = [("path", C.c_int32), ("block_m", C.c_int32), ("capacity", C.c_int64),
                 ("num_blocks", C.c_int32), ("gemm1_cols", C.c_int32), ("gemm2_cols", C.c_int32),
-                ("reserved", C.c_int32), ("workspace_bytes", C.c_int64),
+                ("decode_layer", C.c_int32), ("workspace_bytes", C.c_int64),
                 ("off_sorted_ids", C.c_int64), ("off_expert_ids", C.c_int64),
                 ("off_num_post_padded", C.c_int64), ("off_xq", C.c_int64), ("off_xs", C.c_int64),
                 ("off_inter", C.c_int64), ("off_inter_scale", C.c_int64), ("off_y", C.c_int64)]
@@ -84,6 +85,8 @@ def lib() -> C.CDLL:
         L.moe_forward.argtypes = [C.POINTER(ForwardArgs), vp, i64, vp]
         L.moe_forward_profiled.restype = C.c_int
         L.moe_forward_profiled.argtypes = [C.POINTER(ForwardArgs), vp, i64, vp, C.POINTER(C.c_void_p), i32]
+        L.moe_decode_layer.restype = C.c_int
+        L.moe_decode_layer.argtypes = [C.POINTER(ForwardArgs), vp, i32, vp, vp, vp, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -247,3 +250,45 @@ def moe_forward_profiled(args: ForwardArgs, workspace: torch.Tensor, events, str
     arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
     _check("moe_forward_profiled", lib().moe_forward_profiled(
         C.byref(args), _ptr(workspace), workspace.numel(), C.c_void_p(s.cuda_stream), arr, len(events)))
+
+
+_SYNC = {}
+
+
+def decode_sync(device) -> torch.Tensor:
+    """A zeroed barrier buffer for moe_decode_layer on ``device`` (kept per
+    device and reused: every call leaves it zero)."""
+    key = torch.device(device).index or 0
+    if key not in _SYNC:
+        _SYNC[key] = torch.zeros(MOE_SYNC_WORDS, dtype=torch.int32, device=device)
+    return _SYNC[key]
+
+
+def moe_decode_layer(x, w13, w2, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
+                     router_logits=None, topk=None, renormalize=True, out=None, workspace=None, sync=None,
+                     weight_on_input=False, clamp_limit=0.0):
+    """The layer for few tokens as one kernel launch.  With fp32
+    ``router_logits`` [T,E] it routes them (top ``topk``) into topk_ids /
+    topk_weights (allocated when None); else it uses the given routing.
+    Returns (out, topk_ids, topk_weights, workspace)."""
+    T, H = x.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if router_logits is not None and topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+        topk_weights = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out,
+                     weight_on_input=weight_on_input, clamp_limit=clamp_limit)
+    need = moe_forward_workspace(a)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    sync = decode_sync(dev) if sync is None else sync
+    if router_logits is not None:
+        st = lib().moe_decode_layer(C.byref(a), _ptr(router_logits), int(bool(renormalize)), _ptr(topk_ids),
+                                    _ptr(topk_weights), _ptr(sync), _ptr(workspace), workspace.numel(), _stream(dev))
+    else:
+        st = lib().moe_decode_layer(C.byref(a), None, 0, None, None, _ptr(sync), _ptr(workspace),
+                                    workspace.numel(), _stream(dev))
+    _check("moe_decode_layer", st)
+    return out, topk_ids, topk_weights, workspace

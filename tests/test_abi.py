@@ -202,3 +202,32 @@ def test_route_align_quant_validation():
     assert L.moe_quant_act_mx(f, -1, 32, f, f, None) == ops.MOE_ERR_INVALID_ARG
     assert L.moe_quant_act_mx(C.c_void_p(FAKE + 8), 4, 32, f, f, None) == ops.MOE_ERR_INVALID_ARG
     assert L.moe_quant_act_mx(None, 0, 32, None, None, None) == ops.MOE_OK
+
+
+def test_decode_layer_validation():
+    """moe_decode_layer: shapes outside its scope and missing buffers are
+    rejected on the host before any launch."""
+    L = ops.lib()
+    f = C.c_void_p(FAKE)
+
+    def call(a, logits=None, ids_out=FAKE, w_out=FAKE, sync=FAKE, ws=FAKE, nbytes=1 << 40):
+        return L.moe_decode_layer(C.byref(a), None if logits is None else C.c_void_p(logits), 1,
+                                  None if ids_out is None else C.c_void_p(ids_out),
+                                  None if w_out is None else C.c_void_p(w_out),
+                                  None if sync is None else C.c_void_p(sync),
+                                  None if ws is None else C.c_void_p(ws), nbytes, None)
+    assert ops.moe_plan(_args())["decode_layer"] == 1
+    assert call(_args(T=64)) == ops.MOE_ERR_UNSUPPORTED              # 512 slots
+    assert call(_args(H=4160)) == ops.MOE_ERR_UNSUPPORTED            # H % 256 != 0
+    assert call(_args(block_m=32)) == ops.MOE_ERR_UNSUPPORTED        # only 16-row blocks
+    assert call(_args(path=ops.MOE_PATH_LARGE_M, T=4096)) == ops.MOE_ERR_UNSUPPORTED
+    assert call(_args(), sync=None) == ops.MOE_ERR_INVALID_ARG
+    assert call(_args(), sync=FAKE + 2) == ops.MOE_ERR_INVALID_ARG
+    assert call(_args(), logits=FAKE, ids_out=None) == ops.MOE_ERR_INVALID_ARG
+    assert call(_args(), logits=FAKE, w_out=None) == ops.MOE_ERR_INVALID_ARG
+    assert call(_args(E=4, k=8), logits=FAKE) in (ops.MOE_ERR_INVALID_ARG, ops.MOE_ERR_UNSUPPORTED)
+    assert call(_args(ptr=None)) == ops.MOE_ERR_INVALID_ARG
+    assert call(_args(), ws=None) == ops.MOE_ERR_WORKSPACE
+    assert call(_args(), nbytes=16) == ops.MOE_ERR_WORKSPACE
+    assert call(_args(T=0, ptr=None), sync=None, ws=None) in (ops.MOE_OK, ops.MOE_ERR_INVALID_ARG)
+    del f

@@ -427,3 +427,96 @@ def test_forward_variants_change_the_output():
     for v in ("on_input", "clamp"):
         out, _ = _forward_case(cfg, **_VARIANTS[v])
         assert not torch.equal(out, base), v
+
+
+# ------------------------------------------------- single-launch decode layer ---
+
+def _decode_layer_case(cfg, tokens=None, **kw):
+    """moe_decode_layer (routing inside the kernel when the workload routes
+    from logits) against moe_route + moe_forward on the GPU (bitwise: the same
+    device code) and against the oracle; the barrier buffer must come back
+    zero."""
+    wl = Workload(cfg)
+    ids_o, tw_o, lg = routing(cfg)
+    layer = layer_for(cfg)
+    layer.ensure(np.unique(ids_o))
+    d = dev()
+    x = bits_to_bf16(wl.x_bf16_bits()).to(d)
+    sync = torch.zeros(ops.MOE_SYNC_WORDS, dtype=torch.int32, device=d)
+    log(f"decode layer {cfg.name} T={cfg.T} {cfg.wdtype} {kw}")
+    if lg is not None:
+        lg_t = torch.from_numpy(lg).to(d)
+        out, ids_t, tw_t, _ = ops.moe_decode_layer(x, layer.w13, layer.w2, None, None, layer.s13, layer.s2,
+                                                   router_logits=lg_t, topk=cfg.topk, sync=sync, **kw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids_t.cpu().numpy(), ids_o)
+        w = tw_t.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(w - tw_o) <= route_weight_tol(lg, ids_o, tw_o))
+        ref_ids, ref_tw = ops.moe_route(lg_t, cfg.topk)
+    else:
+        ids_t = torch.from_numpy(np.ascontiguousarray(ids_o, dtype=np.int32)).to(d)
+        tw_t = torch.from_numpy(tw_o.astype(np.float32)).to(d)
+        out, _, _, _ = ops.moe_decode_layer(x, layer.w13, layer.w2, ids_t, tw_t, layer.s13, layer.s2, sync=sync,
+                                            **kw)
+        ref_ids, ref_tw = ids_t, tw_t
+    ref, _ = ops.moe_forward(x, layer.w13, layer.w2, ref_ids, ref_tw, layer.s13, layer.s2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "decode layer differs from moe_forward"
+    assert int(sync.abs().sum()) == 0, sync.cpu().numpy()
+    tokens = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
+    o = oracle_tokens(layer, wl.x_exact(), ids_o, tw_o, tokens, kw.get("weight_on_input", False),
+                      kw.get("clamp_limit", 0.0))
+    excess, raw, _ = compare_output(out.to(torch.float64).cpu().numpy()[tokens], o)
+    log(f"  excess/RMS={excess:.3e} raw max/RMS={raw:.3e}")
+    assert excess <= TAU[cfg.wdtype], (excess, raw)
+    return out
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
+def test_decode_layer_tiny(wdtype):
+    _decode_layer_case(replace(CONFIGS["tiny"], wdtype=wdtype))
+
+
+def test_decode_layer_decode_workload():
+    _decode_layer_case(CONFIGS["decode"])
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 32])
+def test_decode_layer_skew(T):
+    _decode_layer_case(CONFIGS["skew"].with_tokens(T))
+
+
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
+def test_decode_layer_given_routing(wdtype):
+    """fp8 layers at the decode shape with routing handed in (no route phase)."""
+    _decode_layer_case(replace(CONFIGS[wdtype], T=16))
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+def test_decode_layer_variants(wdtype):
+    _decode_layer_case(replace(CONFIGS["tiny"], wdtype=wdtype), **_VARIANTS["both"])
+
+
+def test_decode_layer_repeated_calls_and_plan():
+    """Back-to-back calls on one barrier buffer give the same output and leave
+    it zero; the plan reports where the decode layer applies."""
+    cfg = CONFIGS["decode"]
+    a = ops.forward_args(None, None, None, None, None, shape=(cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk, 0))
+    assert ops.moe_plan(a)["decode_layer"] == 1
+    a = ops.forward_args(None, None, None, None, None, shape=(64, cfg.E, cfg.H, cfg.I, cfg.topk, 0))
+    assert ops.moe_plan(a)["decode_layer"] == 0          # 512 slots: beyond the one-wave alignment
+    wl = Workload(cfg)
+    _, _, lg = routing(cfg)
+    layer = layer_for(cfg)
+    layer.ensure(np.unique(routing(cfg)[0]))
+    d = dev()
+    x = bits_to_bf16(wl.x_bf16_bits()).to(d)
+    lg_t = torch.from_numpy(lg).to(d)
+    sync = torch.zeros(ops.MOE_SYNC_WORDS, dtype=torch.int32, device=d)
+    outs = []
+    for _ in range(3):
+        out, _, _, _ = ops.moe_decode_layer(x, layer.w13, layer.w2, router_logits=lg_t, topk=cfg.topk, sync=sync)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert all(torch.equal(o.view(torch.int16), outs[0].view(torch.int16)) for o in outs)
+    assert int(sync.abs().sum()) == 0
