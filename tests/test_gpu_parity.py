@@ -520,3 +520,58 @@ def test_decode_layer_repeated_calls_and_plan():
     torch.cuda.synchronize()
     assert all(torch.equal(o.view(torch.int16), outs[0].view(torch.int16)) for o in outs)
     assert int(sync.abs().sum()) == 0
+
+
+# ---------------------------------------------------------- extreme shapes ---
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
+def test_forward_max_experts_and_topk(wdtype):
+    """E = 1024 experts and topk = 64 (the ABI limits) with duplicate and
+    unrouted ids; 1280 routed slots take the one-workgroup alignment."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config("maxek", 20, 1024, 256, 128, 64, wdtype, "given")
+    wl = Workload(cfg)
+    rng = np.random.default_rng(23)
+    ids = rng.integers(0, 1024, size=(20, 64)).astype(np.int32)
+    ids[0, :8] = 7                      # one expert taking 8 slots of a token
+    ids[1, 5] = -1
+    ids[2, 9] = 1024
+    tw = rng.random((20, 64)).astype(np.float32) / 64
+    layer = layer_for(cfg)
+    layer.ensure(np.unique(ids[(ids >= 0) & (ids < 1024)]))
+    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw)
+    gpu = out.to(torch.float64).cpu().numpy()
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(20))
+    excess, raw, _ = compare_output(gpu, o)
+    log(f"E=1024 topk=64 {wdtype}: excess/RMS={excess:.3e} raw={raw:.3e}")
+    assert excess <= TAU[wdtype]
+
+
+def test_forward_single_expert_single_token_and_empty_batch():
+    """E = 1, topk = 1, T = 1 (the dense-MLP special case), and T = 0, which
+    must leave the output untouched."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config("e1", 1, 1, 256, 128, 1, "bf16", "given")
+    wl = Workload(cfg)
+    layer = layer_for(cfg)
+    layer.ensure([0])
+    ids = np.zeros((1, 1), np.int32)
+    tw = np.full((1, 1), 0.75, np.float32)
+    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw)
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(1))
+    excess, _, _ = compare_output(out.to(torch.float64).cpu().numpy(), o)
+    assert excess <= TAU["bf16"]
+    d = dev()
+    x0 = torch.empty((0, 256), dtype=torch.bfloat16, device=d)
+    sentinel = torch.full((1, 256), 7.0, dtype=torch.bfloat16, device=d)
+    out0, _ = ops.moe_forward(x0, layer.w13, layer.w2, torch.empty((0, 1), dtype=torch.int32, device=d),
+                              torch.empty((0, 1), dtype=torch.float32, device=d), out=sentinel[:0])
+    torch.cuda.synchronize()
+    assert out0.shape == (0, 256) and bool((sentinel == 7.0).all())
+
+
+def test_decode_layer_max_experts_and_topk():
+    """The single-launch layer at E = 1024, topk = 64 (256 slots, the one-wave
+    alignment's limit), from logits."""
+    from moe_layer_amd.workloads import Config
+    _decode_layer_case(Config("dl_maxek", 4, 1024, 256, 128, 64, "bf16", "logits"))
