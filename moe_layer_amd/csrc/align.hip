@@ -164,6 +164,9 @@ __global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restri
 // ---------------------------------------------------------------------------
 // one-wave form for few slots (decode): no cross-wave synchronisation
 // ---------------------------------------------------------------------------
+// NB 64-slot batches (R <= 64 * NB): less code for fewer slots, which is most
+// of this one-shot kernel's time
+template <int NB>
 __global__ __launch_bounds__(64) void align_tiny_kernel(const int32_t* __restrict__ ids, int R, int E, int B,
                                                        int cap, int32_t* __restrict__ sorted,
                                                        int32_t* __restrict__ expert_ids,
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(64) void align_tiny_kernel(const int32_t* __restric
                                                        int32_t* __restrict__ inv) {
     __shared__ int cnt[kMaxE];
     __shared__ int offs[kMaxE + 1];
-    align_tiny_wg(ids, R, E, B, cap, sorted, expert_ids, ntpp, inv, cnt, offs, true);
+    align_tiny_wg<NB>(ids, R, E, B, cap, sorted, expert_ids, ntpp, inv, cnt, offs, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -365,12 +368,15 @@ __global__ __launch_bounds__(kWideThreads) void align_scatter_kernel(const int32
 hipError_t launch_align(const int32_t* ids, int T, int topk, int E, int block_m, int64_t cap,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, int32_t* inv,
                         hipStream_t s) {
-    if (T * topk <= kTinyMaxSlots)
-        hipLaunchKernelGGL(align_tiny_kernel, dim3(1), dim3(64), 0, s, ids, T * topk, E, block_m, int(cap),
-                           sorted_ids, expert_ids, ntpp, inv);
-    else
-        hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), 0, s, ids, T * topk, E, block_m,
-                           int(cap), sorted_ids, expert_ids, ntpp, inv);
+    const int R = T * topk;
+    if (R <= kTinyMaxSlots) {
+        auto k = R <= 64 ? align_tiny_kernel<1> : R <= 128 ? align_tiny_kernel<2> : align_tiny_kernel<kTinyBatches>;
+        hipLaunchKernelGGL(k, dim3(1), dim3(64), 0, s, ids, R, E, block_m, int(cap), sorted_ids, expert_ids, ntpp,
+                           inv);
+    } else {
+        hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), 0, s, ids, R, E, block_m, int(cap), sorted_ids,
+                           expert_ids, ntpp, inv);
+    }
     return hipGetLastError();
 }
 

@@ -25,21 +25,23 @@ __device__ __forceinline__ uint64_t peers(int e, bool valid, int nbits) {
     return valid ? m : 0ull;
 }
 
-// The alignment of R <= kTinyMaxSlots slots by one wave.  Called by every wave
-// of a workgroup (its barriers are workgroup barriers); only waves with act set
-// do the work, so pass act for exactly one wave.  cnt[kMaxE] and
-// offs[kMaxE + 1] are LDS scratch.
+// The alignment of R <= 64 * NB (NB <= kTinyBatches) slots by one wave.
+// Called by every wave of a workgroup (its barriers are workgroup barriers);
+// only waves with act set do the work, so pass act for exactly one wave.
+// cnt[kMaxE] and offs[kMaxE + 1] are LDS scratch.
+template <int NB = kTinyBatches>
 __device__ __forceinline__ void align_tiny_wg(const int32_t* __restrict__ ids, int R, int E, int B, int cap,
                                               int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
                                               int32_t* __restrict__ ntpp, int32_t* __restrict__ inv, int* cnt,
                                               int* offs, bool act) {
+    static_assert(NB >= 1 && NB <= kTinyBatches, "64-slot batches");
     const int lane = threadIdx.x & 63;
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    int ev[kTinyBatches];
-    uint64_t m[kTinyBatches];
+    int ev[NB];
+    uint64_t m[NB];
 #pragma unroll
-    for (int u = 0; u < kTinyBatches; ++u) {
+    for (int u = 0; u < NB; ++u) {
         const int f = 64 * u + lane;
         ev[u] = act && f < R ? ids[f] : -1;
         m[u] = 0;
@@ -48,7 +50,7 @@ __device__ __forceinline__ void align_tiny_wg(const int32_t* __restrict__ ids, i
         for (int e = lane; e < E; e += 64) cnt[e] = 0;
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kTinyBatches; ++u) {
+    for (int u = 0; u < NB; ++u) {
         if (act) {
             const int e = ev[u];
             const bool valid = e >= 0 && e < E;
@@ -87,7 +89,7 @@ __device__ __forceinline__ void align_tiny_wg(const int32_t* __restrict__ ids, i
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kTinyBatches; ++u) {
+    for (int u = 0; u < NB; ++u) {
         const int f = 64 * u + lane;
         const int e = ev[u];
         const bool valid = e >= 0 && e < E;

@@ -65,18 +65,27 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
     return k;
 }
 
-// Route token t (< T) with the whole calling wave.
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int E, int topk,
-                                            int renormalize, int32_t* __restrict__ ids,
-                                            float* __restrict__ weights, int t) {
+// Experts per lane the routing code is instantiated for: E <= 64 * NPER.
+// Fewer per lane is less code, and these one-shot kernels spend much of their
+// time fetching instructions.
+__host__ __device__ constexpr int route_nper(int E) {
+    return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : kMaxPerLane;
+}
+
+// Route token t (< T) with the whole calling wave; E <= 64 * NPER.
+template <int NPER>
+__device__ __forceinline__ void route_token_n(const float* __restrict__ logits, int E, int topk,
+                                              int renormalize, int32_t* __restrict__ ids,
+                                              float* __restrict__ weights, int t) {
+    static_assert(NPER >= 1 && NPER <= kMaxPerLane, "experts per lane");
     const int lane = threadIdx.x & 63;
     const float* row = logits + int64_t(t) * E;
     const int nper = (E + 63) >> 6;
 
-    float v[kMaxPerLane];
-    uint64_t key[kMaxPerLane];   // 0 = no candidate (below every real key)
+    float v[NPER];
+    uint64_t key[NPER];   // 0 = no candidate (below every real key)
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < NPER; ++i) {
         const int e = lane + 64 * i;
         const bool ok = i < nper && e < E;
         v[i] = ok ? row[e] : 0.0f;
@@ -88,12 +97,12 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     for (int r = 0; r < topk; ++r) {
         uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
+        for (int i = 0; i < NPER; ++i) best = key[i] > best ? key[i] : best;
         const uint64_t w = wave_max_key(best);
         const int wi = int(0xffffu - uint32_t(w & 0xffffu));
         if ((wi & 63) == lane) {
 #pragma unroll
-            for (int i = 0; i < kMaxPerLane; ++i)
+            for (int i = 0; i < NPER; ++i)
                 if (i == (wi >> 6)) key[i] = 0;
         }
         if (lane == r) {
@@ -112,7 +121,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     } else {
         float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
+        for (int i = 0; i < NPER; ++i)
             if (i < nper && lane + 64 * i < E) part = __fadd_rn(part, expf(__fsub_rn(v[i], lmax)));
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) part = __fadd_rn(part, __shfl_xor(part, m));
@@ -122,6 +131,19 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
         const float ex = expf(__fsub_rn(sel_v, lmax));
         ids[int64_t(t) * topk + lane] = sel_i;
         weights[int64_t(t) * topk + lane] = __fdiv_rn(ex, denom);
+    }
+}
+
+// route_token_n for any E <= MOE_MAX_EXPERTS (one instance per experts-per-lane count)
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int E, int topk,
+                                            int renormalize, int32_t* __restrict__ ids,
+                                            float* __restrict__ weights, int t) {
+    switch (route_nper(E)) {
+        case 1: route_token_n<1>(logits, E, topk, renormalize, ids, weights, t); break;
+        case 2: route_token_n<2>(logits, E, topk, renormalize, ids, weights, t); break;
+        case 4: route_token_n<4>(logits, E, topk, renormalize, ids, weights, t); break;
+        case 8: route_token_n<8>(logits, E, topk, renormalize, ids, weights, t); break;
+        default: route_token_n<kMaxPerLane>(logits, E, topk, renormalize, ids, weights, t); break;
     }
 }
 
