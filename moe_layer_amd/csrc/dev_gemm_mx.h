@@ -348,6 +348,120 @@ __device__ __forceinline__ void gemm2_mx_tile(const GemmArgs& g, int blk, int ti
     }
 }
 
+// GEMM2 over NTILE adjacent column tiles of one block in one workgroup: the
+// token-scale table staged once, the K-steps of all tiles one register
+// pipeline (the next tile's loads in flight while the current one is stored).
+// Per tile the arithmetic is gemm2_mx_tile's, so the results are bitwise the
+// same.  Needs I / 128 <= kTabSteps.
+template <int NT, int WT, int NW, int NTILE>
+__device__ __forceinline__ void gemm2_mx_tiles(const GemmArgs& g, int blk, int tile0) {
+    constexpr int MT = WT;
+    constexpr int BM = 16 * NT;
+    constexpr int COLS = NW * WT * 16;
+    const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
+    if (e < 0) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lk = lane >> 4;
+    const int H = g.H, I = g.I, R = g.T * g.topk;
+    const int h0 = tile0 * COLS + wv * WT * 16;
+    const int kbi = I / kMxBlock;
+    const int ns = I / kStepK;
+
+    const uint8_t* w2 = static_cast<const uint8_t*>(g.w2);
+    const uint8_t* w2s = static_cast<const uint8_t*>(g.w2_scale);
+    MxAddr<MT, NT> ad;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int64_t row0 = int64_t(e) * H + h0 + m * 16;
+        ad.a[m] = w2 + row0 * I;
+        ad.as[m] = w2s + row0 * kbi;
+    }
+    ad.aoff = uint32_t(lr * I + lk * 16);
+    ad.asoff = uint32_t(lr * kbi + lk);
+    ad.b = static_cast<const uint8_t*>(g.inter) + int64_t(blk) * BM * I;
+
+    // the block's token-scale table, all of K at once
+    __shared__ __attribute__((aligned(16))) uint8_t tab[BM * kTabStride];
+    {
+        const uint8_t* scales = reinterpret_cast<const uint8_t*>(g.inter_scale) + int64_t(blk) * BM * kbi;
+        for (int i = threadIdx.x; i < BM * ns; i += NW * 64) {
+            const int r = i / ns, k = i - r * ns;
+            *reinterpret_cast<uint32_t*>(tab + r * kTabStride + 4 * k) =
+                *reinterpret_cast<const uint32_t*>(scales + int64_t(r) * kbi + 4 * k);
+        }
+    }
+    int f[NT];
+    float tw[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        ad.boff[n] = uint32_t((n * 16 + lr) * I + lk * 16);
+        ad.bs[n] = tab + (n * 16 + lr) * kTabStride + lk;
+        f[n] = g.sorted_ids[blk * BM + n * 16 + lr];
+        tw[n] = f[n] < R ? gemm2_row_weight(g, f[n]) : 0.0f;
+    }
+    __syncthreads();
+
+    // virtual step v = tile t * ns + k
+    const int64_t tile_bytes = int64_t(COLS) * I;        // weight bytes between tiles
+    const int64_t tile_sbytes = int64_t(COLS) * kbi;     // weight-scale bytes between tiles
+    auto load = [&](MxStage<MT, NT, 1>& st, int v) {
+        const int t = v / ns, k = v - t * ns;
+        const uint32_t off = uint32_t(k) * kStepK;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            st.a[0][m] = ld32<false>(ad.a[m] + t * tile_bytes + (ad.aoff + off));
+            st.sa[0][m] = (ad.as[m] + t * tile_sbytes)[ad.asoff + 4 * k];
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            st.b[0][n] = ld32<false>(ad.b + (ad.boff[n] + off));
+            st.sb[0][n] = ad.bs[n][4 * k];
+        }
+    };
+    f32x4 acc[MT][NT];
+    auto clear = [&]() {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
+    };
+    // after K-step v: a finished tile is scaled by the router weight and stored
+    auto finish = [&](int v) {
+        if ((v + 1) % ns != 0) return;
+        const int hc = h0 + (v / ns) * COLS;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            if (f[n] >= R) continue;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                f32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = __fmul_rn(acc[m][n][j], tw[n]);
+                *reinterpret_cast<f32x4*>(g.y + int64_t(f[n]) * H + hc + m * 16 + 4 * lk) = o;
+            }
+        }
+        clear();
+    };
+
+    clear();
+    const int V = NTILE * ns;
+    MxStage<MT, NT, 1> s0, s1;
+    load(s0, 0);
+    for (int v = 0; v < V; v += 2) {
+        const bool has1 = v + 1 < V;
+        if (has1) load(s1, v + 1);
+        mx_compute<false, MT, NT, 1>(s0, acc);
+        finish(v);
+        if (v + 2 < V) load(s0, v + 2);
+        if (has1) {
+            mx_compute<false, MT, NT, 1>(s1, acc);
+            finish(v + 1);
+        }
+    }
+}
+
 }  // namespace
 
 }  // namespace mx_gemm

@@ -22,6 +22,15 @@ __global__ __launch_bounds__(NW * 64) void gemm2_mx_kernel(GemmArgs g, int ntile
     gemm2_mx_tile<NT, WT, NW>(g, blk, tile);
 }
 
+// GEMM2, NTILE column tiles of one block per workgroup (block-major over the
+// blocks' tile groups)
+template <int NT, int WT, int NW, int NTILE>
+__global__ __launch_bounds__(NW * 64) void gemm2_mx_tiles_kernel(GemmArgs g, int ngroups) {
+    int blk, grp;
+    if (!map_active_tile<true>(g, ngroups, blk, grp)) return;
+    gemm2_mx_tiles<NT, WT, NW, NTILE>(g, blk, grp * NTILE);
+}
+
 template <typename K>
 hipError_t launch_tiles(K kernel, const GemmArgs& g, int ntiles, int threads, hipStream_t s) {
     const int64_t n = int64_t(g.num_blocks) * ntiles;
@@ -38,11 +47,21 @@ hipError_t gemm1_mx(const GemmArgs& g, hipStream_t s) {
     else return launch_tiles(gemm1_mx_kernel<NT, 1, 8>, g, g.I / 128, 512, s);
 }
 
+// Two column tiles per workgroup up to 32-token blocks, four at 64 (the
+// block-fp8 GEMM2's measured choice; the loops are the same).
 template <int NT>
 hipError_t gemm2_mx(const GemmArgs& g, hipStream_t s) {
+    constexpr int kTiles = NT >= 4 ? 4 : 2;
+    const bool multi = g.I / kStepK <= kTabSteps;
     if constexpr (NT <= 2) {
-        if (g.H % 256 == 0) return launch_tiles(gemm2_mx_kernel<NT, 4, 4>, g, g.H / 256, 256, s);
+        if (g.H % 256 == 0) {
+            if (multi && (g.H / 256) % kTiles == 0)
+                return launch_tiles(gemm2_mx_tiles_kernel<NT, 4, 4, kTiles>, g, g.H / 256 / kTiles, 256, s);
+            return launch_tiles(gemm2_mx_kernel<NT, 4, 4>, g, g.H / 256, 256, s);
+        }
     }
+    if (multi && (g.H / 128) % kTiles == 0)
+        return launch_tiles(gemm2_mx_tiles_kernel<NT, 2, 4, kTiles>, g, g.H / 128 / kTiles, 256, s);
     return launch_tiles(gemm2_mx_kernel<NT, 2, 4>, g, g.H / 128, 256, s);
 }
 

@@ -40,8 +40,10 @@ def test_route_workloads(name):
     _check_route(Workload(cfg).logits(), cfg.topk)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 7, 2), (257, 64, 8), (100, 65, 64), (33, 256, 8),
-                                   (17, 1024, 64), (5, 1000, 3)])
+# E across the router's experts-per-lane instances (64, 128, 256, 512, 1024) and their edges
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 7, 2), (257, 64, 8), (100, 65, 64), (9, 128, 8), (9, 129, 8),
+                                   (33, 256, 8), (6, 257, 8), (4, 512, 8), (4, 513, 16), (17, 1024, 64),
+                                   (5, 1000, 3)])
 @pytest.mark.parametrize("renormalize", [True, False])
 def test_route_ties_and_shapes(T, E, k, renormalize):
     rng = np.random.default_rng(T * E + k)
@@ -62,7 +64,9 @@ def _check_align(ids: np.ndarray, E: int, B: int):
     np.testing.assert_array_equal(a["inv"].cpu().numpy(), o["inv"])
 
 
-@pytest.mark.parametrize("T,k,E,B", [(1, 1, 1, 1), (3, 2, 3, 4), (16, 8, 128, 16), (7, 3, 5, 64),
+# slot counts across the one-wave alignment's batch instances (64, 128, 256 slots) and their edges
+@pytest.mark.parametrize("T,k,E,B", [(1, 1, 1, 1), (3, 2, 3, 4), (8, 8, 32, 16), (13, 5, 32, 16), (16, 8, 128, 16),
+                                     (43, 3, 20, 8), (32, 8, 64, 16), (257, 1, 16, 4), (7, 3, 5, 64),
                                      (1024, 8, 256, 32), (4096, 8, 128, 64), (999, 5, 1024, 16),
                                      (50, 4, 9, 1024), (2000, 64, 40, 7)])
 def test_align_random_ids(T, k, E, B):
