@@ -438,21 +438,23 @@ __device__ __forceinline__ void gemm2_small_tile(const GemmArgs& g, int blk, int
     }
 }
 
-// fp8 GEMM2 over NTILE adjacent column tiles of one block in one workgroup.
-// K = I is short (2 K-steps at I = 256), so a one-tile workgroup spends much
+// GEMM2 over NTILE adjacent column tiles of one block in one workgroup.  With
+// a short K (fp8 layer: I = 256, 2 K-steps) a one-tile workgroup spends much
 // of its life on its prologue (token-scale table, first loads) and epilogue
-// (y stores) with no weight bytes in flight.  Here the table is staged once
-// and the K-steps of all NTILE tiles form one register pipeline: the loads of
-// the next tile are in flight while the current one is finished and stored.
-// Per tile the arithmetic is gemm2_small_tile's (same order), so the results
-// are bitwise those of the one-tile form.  Needs I / 128 <= kTabSteps.
-template <int NT, int WT, int NW, int NTILE>
-__device__ __forceinline__ void gemm2_fp8_tiles(const GemmArgs& g, int blk, int tile0) {
-    using O = Op<true>;
+// (y stores) with no weight bytes in flight.  Here the fp8 token-scale table
+// is staged once and the register stages (U K-steps each) of all NTILE tiles
+// form one pipeline: the next tile's loads are in flight while the current
+// one is finished and stored.  Per tile the arithmetic is gemm2_small_tile's
+// (same order), so the results are bitwise those of the one-tile form.  fp8
+// needs I / 128 <= kTabSteps (one table for all of K).
+template <bool FP8, int NT, int WT, int NW, int U, int NTILE>
+__device__ __forceinline__ void gemm2_tiles(const GemmArgs& g, int blk, int tile0) {
+    using O = Op<FP8>;
     constexpr int MT = WT;
     constexpr int BM = 16 * NT;
     constexpr int COLS = NW * WT * 16;
-    static_assert(COLS % kGroup == 0, "a column tile spans whole weight-scale blocks");
+    static_assert(!FP8 || U == 1, "fp8: one K-step per stage");
+    static_assert(!FP8 || COLS % kGroup == 0, "a column tile spans whole weight-scale blocks");
     const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
     if (e < 0) return;
 
@@ -462,7 +464,7 @@ __device__ __forceinline__ void gemm2_fp8_tiles(const GemmArgs& g, int blk, int 
     const int H = g.H, I = g.I, R = g.T * g.topk;
     const int h0 = tile0 * COLS + wv * WT * 16;   // first output row of this wave, first tile
     const int kb_count = I / kGroup;
-    const int ns = I / O::kStepK;                  // K-steps per tile
+    const int ns = I / (O::kStepK * U);            // register stages per tile
 
     const uint8_t* w2 = static_cast<const uint8_t*>(g.w2);
     const uint8_t* inter = static_cast<const uint8_t*>(g.inter);
@@ -473,13 +475,14 @@ __device__ __forceinline__ void gemm2_fp8_tiles(const GemmArgs& g, int blk, int 
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int row = h0 + m * 16;
-        ap[m] = w2 + (int64_t(e) * H + row + lr) * I + lk * O::kLaneOff;
-        asp[m] = static_cast<const float*>(g.w2_scale) + (int64_t(e) * (H / kGroup) + row / kGroup) * kb_count;
+        ap[m] = w2 + (int64_t(e) * H + row + lr) * I * O::kElem + lk * O::kLaneOff;
+        asp[m] = FP8 ? static_cast<const float*>(g.w2_scale) + (int64_t(e) * (H / kGroup) + row / kGroup) * kb_count
+                     : nullptr;
     }
 
-    // the block's token-scale table, all of K at once
-    __shared__ float tab[BM * kTabStride];
-    {
+    // fp8: the block's token-scale table, all of K at once
+    __shared__ float tab[FP8 ? BM * kTabStride : 1];
+    if constexpr (FP8) {
         const float* scales = g.inter_scale + int64_t(blk) * BM * kb_count;
         for (int i = threadIdx.x; i < BM * ns; i += NW * 64) {
             const int r = i / ns, k = i - r * ns;
@@ -491,31 +494,36 @@ __device__ __forceinline__ void gemm2_fp8_tiles(const GemmArgs& g, int blk, int 
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const int row = blk * BM + n * 16 + lr;
-        bp[n] = inter + int64_t(row) * I + lk * O::kLaneOff;
-        bsp[n] = tab + (n * 16 + lr) * kTabStride;
+        bp[n] = inter + int64_t(row) * I * O::kElem + lk * O::kLaneOff;
+        bsp[n] = FP8 ? tab + (n * 16 + lr) * kTabStride : nullptr;
         f[n] = g.sorted_ids[row];
         tw[n] = f[n] < R ? gemm2_row_weight(g, f[n]) : 0.0f;
     }
-    __syncthreads();
+    if constexpr (FP8) __syncthreads();
 
-    // virtual step v = tile t * ns + k
-    const int64_t tile_bytes = int64_t(COLS) * I;             // weight bytes between tiles, per row
-    const int tile_scales = (COLS / kGroup) * kb_count;         // weight-scale words between tiles
-    auto load = [&](Stage<true, MT, NT, 1>& st, int v) {
-        const int t = v / ns, k = v - t * ns;
-        const int64_t off = t * tile_bytes + int64_t(k) * O::kStepBytes;
+    // virtual stage v = tile t * ns + k
+    const int64_t tile_bytes = int64_t(COLS) * I * O::kElem;   // weight bytes between tiles
+    const int tile_scales = (COLS / kGroup) * kb_count;          // fp8 weight-scale words between tiles
+    auto load = [&](Stage<FP8, MT, NT, U>& st, int v) {
+        const int t = v / ns, k = (v - t * ns) * U;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int u = 0; u < U; ++u) {
+            const int64_t off = int64_t(k + u) * O::kStepBytes;
 #pragma unroll
-            for (int p = 0; p < O::kParts; ++p) st.a[0][m][p] = ld16(ap[m] + off + 16 * p);
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+                for (int p = 0; p < O::kParts; ++p) st.a[u][m][p] = ld16(ap[m] + t * tile_bytes + off + 16 * p);
 #pragma unroll
-            for (int p = 0; p < O::kParts; ++p) st.b[0][n][p] = ld16(bp[n] + int64_t(k) * O::kStepBytes + 16 * p);
+            for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) st.sa[0][m] = ld_uniform(asp[m] + t * tile_scales + k);
+                for (int p = 0; p < O::kParts; ++p) st.b[u][n][p] = ld16(bp[n] + off + 16 * p);
+            if constexpr (FP8) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) st.sb[0][n] = bsp[n][k];
+                for (int m = 0; m < MT; ++m) st.sa[u][m] = ld_uniform(asp[m] + t * tile_scales + k + u);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) st.sb[u][n] = bsp[n][k + u];
+            }
+        }
     };
     f32x4 acc[MT][NT];
     auto clear = [&]() {
@@ -524,7 +532,7 @@ __device__ __forceinline__ void gemm2_fp8_tiles(const GemmArgs& g, int blk, int 
 #pragma unroll
             for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
     };
-    // after K-step v: a finished tile is scaled by the router weight and stored
+    // after stage v: a finished tile is scaled by the router weight and stored
     auto finish = [&](int v) {
         if ((v + 1) % ns != 0) return;
         const int hc = h0 + (v / ns) * COLS;
@@ -544,16 +552,16 @@ __device__ __forceinline__ void gemm2_fp8_tiles(const GemmArgs& g, int blk, int 
 
     clear();
     const int V = NTILE * ns;
-    Stage<true, MT, NT, 1> s0, s1;
+    Stage<FP8, MT, NT, U> s0, s1;
     load(s0, 0);
     for (int v = 0; v < V; v += 2) {
         const bool has1 = v + 1 < V;
         if (has1) load(s1, v + 1);
-        compute_stage<true, false, MT, NT, 1>(s0, acc);
+        compute_stage<FP8, false, MT, NT, U>(s0, acc);
         finish(v);
         if (v + 2 < V) load(s0, v + 2);
         if (has1) {
-            compute_stage<true, false, MT, NT, 1>(s1, acc);
+            compute_stage<FP8, false, MT, NT, U>(s1, acc);
             finish(v + 1);
         }
     }

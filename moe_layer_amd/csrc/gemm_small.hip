@@ -27,13 +27,13 @@ __global__ __launch_bounds__(NW * 64) void gemm2_small_kernel(GemmArgs g, int nt
     gemm2_small_tile<FP8, NT, WT, NW, U>(g, blk, tile);
 }
 
-// fp8 GEMM2, NTILE column tiles of one block per workgroup (block-major over
-// the blocks' tile groups)
-template <int NT, int WT, int NW, int NTILE>
-__global__ __launch_bounds__(NW * 64) void gemm2_fp8_tiles_kernel(GemmArgs g, int ngroups) {
+// GEMM2, NTILE column tiles of one block per workgroup (block-major over the
+// blocks' tile groups)
+template <bool FP8, int NT, int WT, int NW, int U, int NTILE>
+__global__ __launch_bounds__(NW * 64) void gemm2_tiles_kernel(GemmArgs g, int ngroups) {
     int blk, grp;
     if (!map_active_tile<true>(g, ngroups, blk, grp)) return;
-    gemm2_fp8_tiles<NT, WT, NW, NTILE>(g, blk, grp * NTILE);
+    gemm2_tiles<FP8, NT, WT, NW, U, NTILE>(g, blk, grp * NTILE);
 }
 
 template <typename K>
@@ -82,7 +82,7 @@ hipError_t gemm2_fp8(const GemmArgs& g, hipStream_t s) {
     constexpr int NW = 4, kTiles = NT >= 4 ? 4 : 2;
     const int ntiles = g.H / (NW * WT * 16);
     if (ntiles % kTiles == 0 && g.I / 128 <= kTabSteps)
-        return launch_tiles(gemm2_fp8_tiles_kernel<NT, WT, NW, kTiles>, g, ntiles / kTiles, NW * 64, s);
+        return launch_tiles(gemm2_tiles_kernel<true, NT, WT, NW, 1, kTiles>, g, ntiles / kTiles, NW * 64, s);
     return launch_tiles(gemm2_small_kernel<true, NT, WT, NW, 1>, g, ntiles, NW * 64, s);
 }
 
