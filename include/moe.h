@@ -280,7 +280,7 @@ MOE_API int moe_forward_profiled(const moe_forward_args* a, void* workspace, int
  * into one, since per-kernel latency is a visible share at a few tokens per
  * step).  Results are bitwise those of moe_route + moe_forward.  On MI355X
  * it measures slower than that pair (one token, 8 of 256 experts, H 7168,
- * I 2048: 0.218 against 0.146 ms): a grid barrier across the 8 XCDs costs
+ * I 2048: 0.215 against 0.141 ms): a grid barrier across the 8 XCDs costs
  * about what a kernel boundary does, and a cooperative launch more than a
  * plain one; it is for callers that need the layer in one launch.
  *

@@ -7,8 +7,8 @@
 // align, combine: a few microseconds each) is a visible share of the layer.
 //
 // Measured on MI355X, this is slower than the kernel-per-stage sequence of
-// moe_forward (one token, 8 of 256 experts, H 7168, I 2048: 0.217 against
-// 0.151 ms): a grid barrier across the 8 XCDs (write-back of the writer's L2,
+// moe_forward (one token, 8 of 256 experts, H 7168, I 2048: 0.215 against
+// 0.141 ms): a grid barrier across the 8 XCDs (write-back of the writer's L2,
 // invalidation of the reader's, cross-XCD atomics) costs about as much as a
 // kernel boundary, the short phases stay latency-bound inside the kernel
 // (route and align take 10-14 us each including their barrier), the GEMM
