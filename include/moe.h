@@ -249,7 +249,9 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  * H % 128 == 0 and I % 128 == 0; MXFP8 also T * H < 2^32 (else
  * MOE_ERR_UNSUPPORTED).  The large-M
  * path needs bf16 weights, H % 256 == 0 and I % 128 == 0; AUTO takes it from
- * 96 routed rows per expert on, forcing it elsewhere is MOE_ERR_UNSUPPORTED.
+ * 12 routed rows per expert (on average) on when min(E, T * topk) * I / 128 >=
+ * 256, unless block_m names a size of the weight-streaming path (16, 32, 64);
+ * forcing it elsewhere is MOE_ERR_UNSUPPORTED.
  * The workspace's activation scales (off_xs, off_inter_scale) are fp32 for
  * FP8_E4M3 and E8M0 bytes for MXFP8.  Unknown flag bits, and a clamp limit
  * that is negative or NaN, are MOE_ERR_INVALID_ARG.

@@ -15,8 +15,17 @@ namespace {
 
 constexpr int kVersionMajor = 1;
 constexpr int kVersionMinor = 3;   // 1.1: MXFP8 weights; 1.2: layer variants; 1.3: moe_decode_layer
-// rows per expert from which the LDS-tiled path beats weight streaming
-constexpr double kLargeMinRowsPerExpert = 96.0;
+// Rows per expert (on average) from which the LDS-tiled path beats weight
+// streaming.  Measured with bf16 weights (align + GEMM1 + GEMM2): E 128, H
+// 4096, I 1536 at 8 rows 0.90 ms streaming vs 1.08 tiled, 16 rows 1.14 vs 1.09,
+// 32 rows 1.49 vs 1.11; E 256, H 7168, I 2048 at 16 rows 5.3 vs 4.9 ms.  The
+// tiled path skips a block's padding-only 32-token sub-tiles, so its 256-row
+// blocks cost little when an expert has few rows.  It also needs enough
+// GEMM1 workgroups (one per expert and 128 intermediate columns) to cover the
+// CUs: on a layer as small as 8 experts, H 256, I 512 (16 rows per expert) the
+// tiled path's 32 workgroups took 0.037 ms against streaming's 0.025.
+constexpr double kLargeMinRowsPerExpert = 12.0;
+constexpr int64_t kLargeMinGemm1Tiles = 256;
 // From this many routed slots on, the alignment runs on many workgroups (one
 // workgroup's ALUs bound it above a few thousand slots).
 constexpr int64_t kAlignWideMinSlots = 2048;
@@ -63,8 +72,12 @@ int make_plan(const moe_forward_args* a, Plan* p) {
     const double rows_per_expert = double(R) / a->E;
     const bool large_ok = gemm_large_supported(a->H, a->I, fp8);
     int path = a->path;
-    if (path == MOE_PATH_AUTO) path = (large_ok && rows_per_expert >= kLargeMinRowsPerExpert) ? MOE_PATH_LARGE_M
-                                                                                              : MOE_PATH_SMALL_M;
+    // AUTO with an explicit block size of the weight-streaming path stays on it
+    const bool bm_ok = a->block_m == 0 || a->block_m == gemm_large_block_m();
+    const bool wide = std::min<int64_t>(a->E, R) * (a->I / 128) >= kLargeMinGemm1Tiles;
+    if (path == MOE_PATH_AUTO)
+        path = (large_ok && bm_ok && wide && rows_per_expert >= kLargeMinRowsPerExpert) ? MOE_PATH_LARGE_M
+                                                                                        : MOE_PATH_SMALL_M;
     int bm = a->block_m;
     if (path == MOE_PATH_LARGE_M) {
         if (!large_ok) return MOE_ERR_UNSUPPORTED;

@@ -267,10 +267,11 @@ def decode_sync(device) -> torch.Tensor:
 def moe_decode_layer(x, w13, w2, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
                      router_logits=None, topk=None, renormalize=True, out=None, workspace=None, sync=None,
                      weight_on_input=False, clamp_limit=0.0):
-    """The layer for few tokens as one kernel launch.  With fp32
-    ``router_logits`` [T,E] it routes them (top ``topk``) into topk_ids /
-    topk_weights (allocated when None); else it uses the given routing.
-    Returns (out, topk_ids, topk_weights, workspace)."""
+    """The layer for few tokens as one kernel launch (the weight-streaming
+    path with 16-row blocks).  With fp32 ``router_logits`` [T,E] it routes
+    them (top ``topk``) into topk_ids / topk_weights (allocated when None);
+    else it uses the given routing.  Returns (out, topk_ids, topk_weights,
+    workspace)."""
     T, H = x.shape
     dev = x.device
     if out is None:
@@ -278,7 +279,7 @@ def moe_decode_layer(x, w13, w2, topk_ids=None, topk_weights=None, w13_scale=Non
     if router_logits is not None and topk_ids is None:
         topk_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
         topk_weights = torch.empty((T, topk), dtype=torch.float32, device=dev)
-    a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out,
+    a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out, MOE_PATH_SMALL_M, 16,
                      weight_on_input=weight_on_input, clamp_limit=clamp_limit)
     need = moe_forward_workspace(a)
     if workspace is None or workspace.numel() < need:

@@ -74,8 +74,11 @@ def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAK
 @pytest.mark.parametrize("T,E,k,wdtype,expect_bm,expect_path", [
     (16, 128, 8, 0, 16, ops.MOE_PATH_SMALL_M),      # decode: 1 row per expert
     (1024, 256, 8, 1, 32, ops.MOE_PATH_SMALL_M),    # fp8: 32 rows per expert
-    (64, 8, 2, 0, 16, ops.MOE_PATH_SMALL_M),        # tiny: 16 rows per expert
-    (512, 64, 8, 0, 64, ops.MOE_PATH_SMALL_M),      # 64 rows per expert
+    (128, 128, 8, 0, 16, ops.MOE_PATH_SMALL_M),     # 8 rows per expert: weight streaming
+    (176, 128, 8, 0, 16, ops.MOE_PATH_SMALL_M),     # 11 rows per expert
+    (192, 128, 8, 0, 256, ops.MOE_PATH_LARGE_M),    # 12 rows per expert: LDS-tiled from here on
+    (64, 8, 2, 0, 16, ops.MOE_PATH_SMALL_M),        # tiny: 16 rows per expert, too few tiles for the LDS path
+    (512, 64, 8, 0, 256, ops.MOE_PATH_LARGE_M),     # 64 rows per expert
     (4096, 128, 8, 0, 256, ops.MOE_PATH_LARGE_M),   # prefill: 256 rows per expert
     (1024, 256, 8, 2, 32, ops.MOE_PATH_SMALL_M),    # MXFP8: 32 rows per expert
     (8192, 256, 8, 2, 64, ops.MOE_PATH_SMALL_M),    # MXFP8 has no large-M path
@@ -122,6 +125,9 @@ def test_plan_large_path_limits():
     assert L.moe_plan(C.byref(_args(path=ops.MOE_PATH_LARGE_M, block_m=64)), C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
     assert L.moe_plan(C.byref(_args(path=ops.MOE_PATH_SMALL_M, block_m=256)), C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
     assert L.moe_plan(C.byref(_args(block_m=128)), C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
+    # AUTO with a weight-streaming block size stays on that path
+    p = ops.moe_plan(_args(T=4096, block_m=32))
+    assert p["path"] == ops.MOE_PATH_SMALL_M and p["block_m"] == 32
     # AUTO falls back to the weight-streaming path where the large one cannot run
     assert ops.moe_plan(_args(T=4096, H=4160))["path"] == ops.MOE_PATH_SMALL_M
     assert ops.moe_plan(_args(T=8192, wdtype=1, I=256))["path"] == ops.MOE_PATH_SMALL_M

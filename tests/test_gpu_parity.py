@@ -463,7 +463,8 @@ def _decode_layer_case(cfg, tokens=None, **kw):
         out, _, _, _ = ops.moe_decode_layer(x, layer.w13, layer.w2, ids_t, tw_t, layer.s13, layer.s2, sync=sync,
                                             **kw)
         ref_ids, ref_tw = ids_t, tw_t
-    ref, _ = ops.moe_forward(x, layer.w13, layer.w2, ref_ids, ref_tw, layer.s13, layer.s2, **kw)
+    ref, _ = ops.moe_forward(x, layer.w13, layer.w2, ref_ids, ref_tw, layer.s13, layer.s2,
+                             path=ops.MOE_PATH_SMALL_M, block_m=16, **kw)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "decode layer differs from moe_forward"
     assert int(sync.abs().sum()) == 0, sync.cpu().numpy()
