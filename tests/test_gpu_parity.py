@@ -248,6 +248,20 @@ def test_prefill_takes_the_large_path():
     assert p["path"] == ops.MOE_PATH_LARGE_M and p["block_m"] == 256
 
 
+@pytest.mark.parametrize("path,block_m", [(ops.MOE_PATH_AUTO, 0), (ops.MOE_PATH_AUTO, 32), (ops.MOE_PATH_SMALL_M, 64)])
+def test_forward_mid_batch(path, block_m):
+    """32 rows per expert: AUTO takes the LDS-tiled path (256-row blocks, most
+    32-token sub-tiles padding-only), an explicit 32-row block keeps AUTO on the
+    weight-streaming path; every form matches the oracle."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config("midbatch", 256, 64, 512, 512, 8, "bf16", "logits")
+    a = ops.forward_args(None, None, None, None, None, shape=(cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk, 0),
+                         path=path, block_m=block_m)
+    want = ops.MOE_PATH_LARGE_M if (path, block_m) == (ops.MOE_PATH_AUTO, 0) else ops.MOE_PATH_SMALL_M
+    assert ops.moe_plan(a)["path"] == want
+    _forward_case(cfg, path=path, block_m=block_m)
+
+
 def test_forward_prefill_small_path_sampled():
     rng = np.random.default_rng(7)
     _forward_case(CONFIGS["prefill"], tokens=np.sort(rng.choice(4096, 64, replace=False)),
