@@ -56,8 +56,12 @@ static_assert(kLoads * kLoadRows == 256, "the loader must cover the 256 tile row
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-template <int GEMM, int NU>
-__device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int blk, int tile, int e) {
+// valid: the block's real rows (a prefix).  kSkip: token rows of whole load
+// steps past it are neither loaded nor written to LDS (only padding-only
+// sub-tiles read those rows, and they are not multiplied); the other form
+// keeps its loads unconditional.
+template <int GEMM, int NU, bool kSkip>
+__device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int blk, int tile, int e, int valid) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -95,7 +99,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
             ra[j] = *reinterpret_cast<const i32x4*>(a_src[j] + off);
-            rb[j] = *reinterpret_cast<const i32x4*>(b_src[j] + off);
+            if (!kSkip || j * kLoadRows < valid) rb[j] = *reinterpret_cast<const i32x4*>(b_src[j] + off);
         }
     };
     auto lstore = [&](int buf) {
@@ -104,7 +108,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
             *reinterpret_cast<i32x4*>(A + swz(j * kLoadRows + row0, chunk)) = ra[j];
-            *reinterpret_cast<i32x4*>(B + swz(j * kLoadRows + row0, chunk)) = rb[j];
+            if (!kSkip || j * kLoadRows < valid)
+                *reinterpret_cast<i32x4*>(B + swz(j * kLoadRows + row0, chunk)) = rb[j];
         }
     };
 
@@ -225,12 +230,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
     // live 32-token sub-tiles of this wave: u = wn, wn + 2, ... below the count
     const int live = (s_valid + 31) >> 5;
     const int wn = (threadIdx.x >> 6) / kWM;
-    switch ((live - wn + 1) >> 1) {
-        case 0: run_tile<GEMM, 0>(g, lds, blk, tile, e); break;
-        case 1: run_tile<GEMM, 1>(g, lds, blk, tile, e); break;
-        case 2: run_tile<GEMM, 2>(g, lds, blk, tile, e); break;
-        case 3: run_tile<GEMM, 3>(g, lds, blk, tile, e); break;
-        default: run_tile<GEMM, 4>(g, lds, blk, tile, e); break;
+    const int nu = (live - wn + 1) >> 1;
+    if constexpr (GEMM == 2) {
+        // GEMM2 reads the intermediate's padding rows from memory: a block with
+        // a whole token load step of padding (at most 6 live sub-tiles, 0..3
+        // per wave) skips them (the down GEMM of 16-64 rows per expert 5-14 %
+        // faster); a fuller block has 3 or 4 per wave.  GEMM1's padding rows
+        // all read token 0, which stays in L2: it gained nothing there.
+        if (s_valid <= kBM - kLoadRows) {
+            switch (nu) {
+                case 0: run_tile<GEMM, 0, true>(g, lds, blk, tile, e, s_valid); break;
+                case 1: run_tile<GEMM, 1, true>(g, lds, blk, tile, e, s_valid); break;
+                case 2: run_tile<GEMM, 2, true>(g, lds, blk, tile, e, s_valid); break;
+                default: run_tile<GEMM, 3, true>(g, lds, blk, tile, e, s_valid); break;
+            }
+        } else if (nu >= 4) {
+            run_tile<GEMM, 4, false>(g, lds, blk, tile, e, s_valid);
+        } else {
+            run_tile<GEMM, 3, false>(g, lds, blk, tile, e, s_valid);
+        }
+    } else {
+        switch (nu) {
+            case 0: run_tile<GEMM, 0, false>(g, lds, blk, tile, e, s_valid); break;
+            case 1: run_tile<GEMM, 1, false>(g, lds, blk, tile, e, s_valid); break;
+            case 2: run_tile<GEMM, 2, false>(g, lds, blk, tile, e, s_valid); break;
+            case 3: run_tile<GEMM, 3, false>(g, lds, blk, tile, e, s_valid); break;
+            default: run_tile<GEMM, 4, false>(g, lds, blk, tile, e, s_valid); break;
+        }
     }
 }
 
