@@ -8,10 +8,11 @@
 // sub-tiles u (32 rows each) with u % 2 == wn, so the live sub-tiles of a
 // block's partly filled tail split evenly between the two waves of a SIMD.
 // K is walked in stages of 64: both operand tiles of the next stage (256x64
-// bf16 each, 64 KiB) are loaded into registers while the current stage is
-// multiplied from LDS, then written to the other of two LDS buffers; one
-// barrier per stage (32 MFMAs per wave).  Every LDS access is ordinary code,
-// so the compiler interleaves the fragment reads with the MFMAs.
+// bf16 each, 64 KiB; 320 token rows with a following short block, below) are
+// loaded into registers while the current stage is multiplied from LDS, then
+// written to the other of two LDS buffers; one barrier per stage (32 MFMAs per
+// wave).  Every LDS access is ordinary code, so the compiler interleaves the
+// fragment reads with the MFMAs.
 //
 // LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r sits at
 // position c ^ ((r >> 1) & 7), which spreads the 32 rows a fragment read
@@ -23,7 +24,13 @@
 //
 // Token sub-tiles that hold only padding (the tail of an expert's last block)
 // are neither multiplied nor stored: the main loop is instantiated per wave for
-// 0..4 live sub-tiles.
+// 0..4 live sub-tiles.  An expert's last block with at most 64 real rows is
+// taken by the workgroup of the expert's previous (full) block as token rows
+// 256..319 (sub-tiles 8 and 9, so 4 or 5 per wave): the expert's weight tiles
+// stream once for both blocks.  With routing near 256 rows per expert about
+// half of the experts end in such a block, which otherwise re-streams every
+// weight tile for a few rows (prefill layer: 1.52x the algorithmic HBM bytes;
+// GEMM1 1.28 -> 1.20 ms, GEMM2 0.69 -> 0.66 ms).
 //
 //   GEMM1 (a4+a5): tile = 128 intermediate columns: gate rows c0..c0+127 and
 //                  up rows I+c0..; wave (wm, .) owns gate rows c0+32wm.. and
@@ -48,11 +55,16 @@ constexpr int kWaves = 2 * kWM;                // x 2 along the tokens
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTW = kTM / kWM;                 // weight rows per wave
 constexpr int kTA = kTW / 32;                  // 32-row A fragments per wave
-constexpr int kTileBytes = 256 * kRowBytes;         // one operand stage: 32 KiB
-constexpr int kStageBytes = 2 * kTileBytes;         // weights + tokens
-constexpr int kLoads = kTileBytes / 16 / kThreads;  // 16-byte loads per thread per operand
+constexpr int kXR = 64;            // rows a workgroup may take from the expert's next block
+constexpr int kBR = kBM + kXR;     // token rows of the LDS token tile
+constexpr int kTileBytes = kTM * kRowBytes;         // weight stage: 32 KiB
+constexpr int kBTileBytes = kBR * kRowBytes;        // token stage: 40 KiB
+constexpr int kStageBytes = kTileBytes + kBTileBytes;
+constexpr int kLoads = kTileBytes / 16 / kThreads;  // 16-byte loads per thread per weight stage
 constexpr int kLoadRows = kThreads / 8;              // tile rows one load step covers (8 chunks a row)
-static_assert(kLoads * kLoadRows == 256, "the loader must cover the 256 tile rows exactly once");
+constexpr int kLoadsB = kBR / kLoadRows;             // token load steps with the next block's rows
+static_assert(kLoads * kLoadRows == kTM, "the loader must cover the weight tile rows exactly once");
+static_assert(kLoadsB == kLoads + 1 && kXR == kLoadRows, "the next block's rows take one token load step");
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -60,7 +72,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes 
 // steps past it are neither loaded nor written to LDS (only padding-only
 // sub-tiles read those rows, and they are not multiplied); the other form
 // keeps its loads unconditional.
-template <int GEMM, int NU, bool kSkip>
+template <int GEMM, int NU, bool kSkip, bool kExt>
 __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int blk, int tile, int e, int valid) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -74,31 +86,37 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
     // ---- global sources: thread tid moves chunk (tid & 7) of rows j*kLoadRows + tid/8
     const int chunk = tid & 7;
     const int row0 = tid >> 3;   // 0..kLoadRows-1
+    constexpr int kLB = kExt ? kLoadsB : kLoads;   // token load steps
     const uint8_t* a_src[kLoads];
-    const uint8_t* b_src[kLoads];
+    const uint8_t* b_src[kLB];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        const int r = j * kLoadRows + row0;   // tile row 0..255
+    for (int j = 0; j < kLB; ++j) {
+        const int r = j * kLoadRows + row0;   // tile row 0..255 (token rows to 319 with kExt)
         if constexpr (GEMM == 1) {
             // tile row r = kTW*w + (kTW/2)*half + rr: weight-wave w's gate rows, then its up rows
-            const int half = (r / (kTW / 2)) & 1, rr = r % (kTW / 2);
-            const int64_t grow = int64_t(e) * 2 * g.I + (half ? g.I : 0) + tile * 128 + (r / kTW) * (kTW / 2) + rr;
-            a_src[j] = static_cast<const uint8_t*>(g.w13) + grow * kbytes + chunk * 16;
+            if (j < kLoads) {
+                const int half = (r / (kTW / 2)) & 1, rr = r % (kTW / 2);
+                const int64_t grow =
+                    int64_t(e) * 2 * g.I + (half ? g.I : 0) + tile * 128 + (r / kTW) * (kTW / 2) + rr;
+                a_src[j] = static_cast<const uint8_t*>(g.w13) + grow * kbytes + chunk * 16;
+            }
             const int f = g.sorted_ids[blk * kBM + r];
             const int tok = f < R ? f / g.topk : 0;   // padding rows read token 0 (never stored as real rows)
             b_src[j] = reinterpret_cast<const uint8_t*>(g.x) + int64_t(tok) * kbytes + chunk * 16;
         } else {
-            const int64_t grow = int64_t(e) * g.H + tile * kTM + r;
-            a_src[j] = static_cast<const uint8_t*>(g.w2) + grow * kbytes + chunk * 16;
+            if (j < kLoads) {
+                const int64_t grow = int64_t(e) * g.H + tile * kTM + r;
+                a_src[j] = static_cast<const uint8_t*>(g.w2) + grow * kbytes + chunk * 16;
+            }
             b_src[j] = static_cast<const uint8_t*>(g.inter) + int64_t(blk * kBM + r) * kbytes + chunk * 16;
         }
     }
-    i32x4 ra[kLoads], rb[kLoads];
+    i32x4 ra[kLoads], rb[kLB];
     auto gload = [&](int st) {
         const int64_t off = int64_t(st) * kRowBytes;
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            ra[j] = *reinterpret_cast<const i32x4*>(a_src[j] + off);
+        for (int j = 0; j < kLB; ++j) {
+            if (j < kLoads) ra[j] = *reinterpret_cast<const i32x4*>(a_src[j] + off);
             if (!kSkip || j * kLoadRows < valid) rb[j] = *reinterpret_cast<const i32x4*>(b_src[j] + off);
         }
     };
@@ -106,8 +124,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, uint8_t* lds, int bl
         uint8_t* A = lds + buf * kStageBytes;
         uint8_t* B = A + kTileBytes;
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            *reinterpret_cast<i32x4*>(A + swz(j * kLoadRows + row0, chunk)) = ra[j];
+        for (int j = 0; j < kLB; ++j) {
+            if (j < kLoads) *reinterpret_cast<i32x4*>(A + swz(j * kLoadRows + row0, chunk)) = ra[j];
             if (!kSkip || j * kLoadRows < valid)
                 *reinterpret_cast<i32x4*>(B + swz(j * kLoadRows + row0, chunk)) = rb[j];
         }
@@ -218,12 +236,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
     const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
     if (e < 0) return;
 
-    // rows of this block that hold real slots (a prefix: padding sits at the end)
+    // An expert's last block with at most kXR real rows (row kXR is padding)
+    // rides along with the expert's previous block: that workgroup multiplies
+    // its rows as token rows 256..319 of the same weight tiles, so the expert's
+    // weights stream once for both (each output keeps its K order: results are
+    // the same bits).
     const int R = g.T * g.topk;
+    const int active = __builtin_amdgcn_readfirstlane(g.ntpp[0]) / kBM;
+    auto short_tail = [&](int b) { return g.sorted_ids[b * kBM + kXR] >= R; };
+    if (blk > 0 && g.expert_ids[blk - 1] == e && short_tail(blk)) return;
+    const bool ext = blk + 1 < active && g.expert_ids[blk + 1] == e && short_tail(blk + 1);
+
+    // rows of the token tile that hold real slots (a prefix: padding sits at the end)
     if (threadIdx.x < 64) {
         int n = 0;
 #pragma unroll
-        for (int q = 0; q < kBM / 64; ++q) n += __popcll(__ballot(g.sorted_ids[blk * kBM + q * 64 + threadIdx.x] < R));
+        for (int q = 0; q < kBR / 64; ++q)
+            if (q < kBM / 64 || ext) n += __popcll(__ballot(g.sorted_ids[blk * kBM + q * 64 + threadIdx.x] < R));
         if (threadIdx.x == 0) s_valid = n;
     }
     __syncthreads();
@@ -231,6 +260,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
     const int live = (s_valid + 31) >> 5;
     const int wn = (threadIdx.x >> 6) / kWM;
     const int nu = (live - wn + 1) >> 1;
+    if (ext) {   // 257..320 rows: 4 or 5 sub-tiles per wave
+        if (nu >= 5) run_tile<GEMM, 5, false, true>(g, lds, blk, tile, e, s_valid);
+        else run_tile<GEMM, 4, false, true>(g, lds, blk, tile, e, s_valid);
+        return;
+    }
     if constexpr (GEMM == 2) {
         // GEMM2 reads the intermediate's padding rows from memory: a block with
         // a whole token load step of padding (at most 6 live sub-tiles, 0..3
@@ -239,23 +273,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(GemmArgs g, int
         // all read token 0, which stays in L2: it gained nothing there.
         if (s_valid <= kBM - kLoadRows) {
             switch (nu) {
-                case 0: run_tile<GEMM, 0, true>(g, lds, blk, tile, e, s_valid); break;
-                case 1: run_tile<GEMM, 1, true>(g, lds, blk, tile, e, s_valid); break;
-                case 2: run_tile<GEMM, 2, true>(g, lds, blk, tile, e, s_valid); break;
-                default: run_tile<GEMM, 3, true>(g, lds, blk, tile, e, s_valid); break;
+                case 0: run_tile<GEMM, 0, true, false>(g, lds, blk, tile, e, s_valid); break;
+                case 1: run_tile<GEMM, 1, true, false>(g, lds, blk, tile, e, s_valid); break;
+                case 2: run_tile<GEMM, 2, true, false>(g, lds, blk, tile, e, s_valid); break;
+                default: run_tile<GEMM, 3, true, false>(g, lds, blk, tile, e, s_valid); break;
             }
         } else if (nu >= 4) {
-            run_tile<GEMM, 4, false>(g, lds, blk, tile, e, s_valid);
+            run_tile<GEMM, 4, false, false>(g, lds, blk, tile, e, s_valid);
         } else {
-            run_tile<GEMM, 3, false>(g, lds, blk, tile, e, s_valid);
+            run_tile<GEMM, 3, false, false>(g, lds, blk, tile, e, s_valid);
         }
     } else {
         switch (nu) {
-            case 0: run_tile<GEMM, 0, false>(g, lds, blk, tile, e, s_valid); break;
-            case 1: run_tile<GEMM, 1, false>(g, lds, blk, tile, e, s_valid); break;
-            case 2: run_tile<GEMM, 2, false>(g, lds, blk, tile, e, s_valid); break;
-            case 3: run_tile<GEMM, 3, false>(g, lds, blk, tile, e, s_valid); break;
-            default: run_tile<GEMM, 4, false>(g, lds, blk, tile, e, s_valid); break;
+            case 0: run_tile<GEMM, 0, false, false>(g, lds, blk, tile, e, s_valid); break;
+            case 1: run_tile<GEMM, 1, false, false>(g, lds, blk, tile, e, s_valid); break;
+            case 2: run_tile<GEMM, 2, false, false>(g, lds, blk, tile, e, s_valid); break;
+            case 3: run_tile<GEMM, 3, false, false>(g, lds, blk, tile, e, s_valid); break;
+            default: run_tile<GEMM, 4, false, false>(g, lds, blk, tile, e, s_valid); break;
         }
     }
 }

@@ -241,6 +241,36 @@ def test_forward_ragged_large_path():
     assert excess <= TAU["bf16"]
 
 
+def test_forward_large_path_short_tail_blocks():
+    """The LDS-tiled path where an expert's last 256-row block holds 1, 32, 33
+    or 64 rows (taken by the workgroup of the expert's previous block as token
+    rows 256..319), 65 rows (a block of its own), a three-block expert whose
+    third block is short, an expert of exactly one full block and a small one;
+    every token compared with the oracle."""
+    from moe_layer_amd.workloads import Config
+    counts = [257, 288, 289, 320, 321, 576, 256, 5]
+    k = 2
+    T = sum(counts) // k
+    cfg = Config("short_tails", T, len(counts), 512, 384, k, "bf16", "given")
+    wl = Workload(cfg)
+    rng = np.random.default_rng(8)
+    slots = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    ids = rng.permutation(slots).reshape(T, k)
+    tw = rng.random((T, k)).astype(np.float32)
+    layer = layer_for(cfg)
+    layer.ensure(range(len(counts)))
+    plan = ops.moe_plan(ops.forward_args(None, None, None, None, None, path=ops.MOE_PATH_LARGE_M,
+                                         shape=(T, len(counts), 512, 384, k, 0)))
+    assert plan["block_m"] == 256
+    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_LARGE_M)
+    gpu = out.to(torch.float64).cpu().numpy()
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(T))
+    excess, raw, _ = compare_output(gpu, o)
+    log(f"short tails: excess/RMS={excess:.3e} raw={raw:.3e}")
+    assert np.all(np.isfinite(gpu))
+    assert excess <= TAU["bf16"]
+
+
 def test_prefill_takes_the_large_path():
     cfg = CONFIGS["prefill"]
     a = ops.forward_args(None, None, None, None, None, shape=(cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk, 0))
