@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="use the first T tokens of the workload")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--path", type=int, default=0)
+    ap.add_argument("--mx-row-major-scales", action="store_true",
+                    help="MXFP8: pass the weight scales row-major instead of packed by moe_pack_mx_scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-layer", action="store_true",
                     help="run each step as one moe_decode_layer launch (routing inside the kernel)")
@@ -168,7 +170,13 @@ def main():
     log(f"weights ready in {time.time() - t0:.1f}s")
 
     out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
-    fargs = ops.forward_args(x, w13, w2, ids, tw, s13, s2, out, args.path, args.block_m)
+    # MXFP8 scales: repacked once with the weights (a static weight conversion,
+    # outside the timed region) unless the row-major layout is asked for
+    packed = mx and not args.mx_row_major_scales
+    if packed:
+        s13, s2 = ops.moe_pack_mx_scales(s13), ops.moe_pack_mx_scales(s2)
+        torch.cuda.synchronize()
+    fargs = ops.forward_args(x, w13, w2, ids, tw, s13, s2, out, args.path, args.block_m, mx_packed_scales=packed)
     plan = ops.moe_plan(fargs)
     ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=d)
     lib = ops.lib()
@@ -297,6 +305,7 @@ def main():
                    "block_m": plan["block_m"], "path": ["auto", "small_m", "large_m"][plan["path"]],
                    "gemm1_mfma": "bf16", "gemm2_mfma": cfg.wdtype,
                    "launch": "one decode-layer kernel" if use_dl else "one kernel per stage",
+                   **({"mx_scales": "packed" if packed else "row-major"} if mx else {}),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -60,8 +60,10 @@ extern "C" {
 #define MOE_PATH_SMALL_M     1   /* weight-streaming path: few rows per expert (decode) */
 #define MOE_PATH_LARGE_M     2   /* LDS-tiled path: many rows per expert (prefill) */
 
-/* layer variants (moe_forward_args.flags) */
+/* layer variants and operand layouts (moe_forward_args.flags) */
 #define MOE_FLAG_WEIGHT_ON_INPUT 1   /* router weight on GEMM1's input, none after GEMM2 */
+#define MOE_FLAG_MX_PACKED_SCALES 2  /* MXFP8 only: w13_scale and w2_scale are in the
+                                        layout moe_pack_mx_scales writes */
 
 /* limits */
 #define MOE_MAX_EXPERTS      1024
@@ -166,6 +168,30 @@ MOE_API int moe_quant_act(const void* x, int32_t rows, int32_t cols, uint8_t* co
 MOE_API int moe_quant_act_mx(const void* x, int32_t rows, int32_t cols, uint8_t* codes,
                              uint8_t* scales, hipStream_t stream);
 
+/*
+ * moe_pack_mx_scales — reorder an MXFP8 weight's E8M0 scale bytes (P3's MXFP8
+ * scheme: one scale per weight row and 32 consecutive K elements) for the
+ * matrix-core kernels, once per weight as part of its static conversion.  The
+ * kernels multiply 16 weight rows by 128 K elements per step, and each of a
+ * wave's 64 lanes needs the scale of one row (lane % 16) and one 32-element
+ * block (lane / 16); in the row-major layout those 64 bytes lie on 16 rows,
+ * packed they are contiguous in lane order:
+ *   packed[((e * rows/16 + t) * K/128 + s) * 64 + g * 16 + r]
+ *       = scales[(e * rows + 16 t + r) * K/32 + 4 s + g]
+ * for r < 16 and g < 4.  Every 16-row group keeps its byte range, so the
+ * packed array has the row-major one's size and offsets at 16-row bounds.
+ * Pass the results as w13_scale / w2_scale with MOE_FLAG_MX_PACKED_SCALES.
+ *
+ *   scales  device, E8M0 bytes [E, rows, K / 32] (row-major)
+ *   packed  device, E8M0 bytes, E * rows * K / 32 of them (output; must not
+ *           overlap scales)
+ * Requires E >= 1, rows % 16 == 0 (w13: rows = 2I; w2: rows = H) and
+ * K % 128 == 0 (w13: K = H; w2: K = I); else MOE_ERR_UNSUPPORTED (sizes) or
+ * MOE_ERR_INVALID_ARG (null pointers, overlap, negative sizes).
+ */
+MOE_API int moe_pack_mx_scales(const uint8_t* scales, int32_t E, int32_t rows, int32_t K, uint8_t* packed,
+                               hipStream_t stream);
+
 /* Arguments of moe_forward (the pages' `apply(x, w1, w2, topk_weights,
  * topk_ids, activation=SiLU, expert_map=None,
  * apply_router_weight_on_input=False)`, P2 section 1.1). */
@@ -179,10 +205,13 @@ typedef struct moe_forward_args {
     const void* x;        /* device bf16 [T, H] */
     const void* w13;      /* device [E, 2I, H]: rows [0, I) gate, [I, 2I) up */
     const void* w13_scale;  /* FP8_E4M3: device fp32 [E, 2I/128, H/128];
-                               MXFP8: device E8M0 bytes [E, 2I, H/32]; else NULL */
+                               MXFP8: device E8M0 bytes [E, 2I, H/32] (packed
+                               by moe_pack_mx_scales with
+                               MOE_FLAG_MX_PACKED_SCALES); else NULL */
     const void* w2;       /* device [E, H, I] */
     const void* w2_scale;   /* FP8_E4M3: device fp32 [E, H/128, I/128];
-                               MXFP8: device E8M0 bytes [E, H, I/32]; else NULL */
+                               MXFP8: device E8M0 bytes [E, H, I/32] (packed
+                               as w13_scale); else NULL */
     const int32_t* topk_ids;   /* device int32 [T, topk] */
     const float* topk_weights; /* device fp32 [T, topk] */
     void* out;            /* device bf16 [T, H] (output) */
@@ -241,6 +270,10 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  *       the bf16 rounding of h, and GEMM2's rows are left unweighted;
  *   clamp_limit L > 0  after their bf16 rounding the gate is capped at L and
  *       the up value held to [-L, L] before the SiLU-gated multiply.
+ * MOE_FLAG_MX_PACKED_SCALES (MXFP8 only, else MOE_ERR_INVALID_ARG): both
+ *       weight-scale arrays are in moe_pack_mx_scales's layout; the results
+ *       are bitwise those of the row-major layout, and the weight-streaming
+ *       kernels read the scales with one coalesced load per tile and step.
  *
  *   workspace  device buffer of at least moe_forward_workspace(a) bytes,
  *              256-byte aligned; its contents on entry do not matter and on

@@ -166,6 +166,7 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* code
                             hipStream_t s);
 hipError_t launch_quant_act_mx(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);
+hipError_t launch_pack_mx_scales(const uint8_t* scales, int E, int rows, int K, uint8_t* packed, hipStream_t s);
 
 struct GemmArgs {
     int T, E, H, I, topk, block_m, num_blocks;
@@ -184,6 +185,7 @@ struct GemmArgs {
     float* inter_scale;         // fp32 [cap, I/128] (fp8) or E8M0 bytes [cap, I/32] (MXFP8)
     float* y;                   // fp32 [T*topk, H]
     int weight_on_input;        // router weight on GEMM1's input instead of GEMM2's output
+    int mx_packed;              // MXFP8 weight scales in the tile-packed layout (moe_pack_mx_scales)
     int clamp;                  // SwiGLU clamp on (limit clamp_limit)
     float clamp_limit;
 };

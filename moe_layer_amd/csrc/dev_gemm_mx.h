@@ -65,19 +65,32 @@ struct MxStage {
 // plus one 32-bit lane offset shared by all weight tiles, so the loads take
 // the scalar-base + vector-offset form and few vector registers hold
 // addresses.  Tokens: one uniform base plus a 32-bit offset per token tile.
-// Weight scales are read per lane (one byte per tile and step; staging them
-// in LDS as well measured no faster); the tokens' scales come from an LDS
-// table the workgroup fills per chunk of kTabSteps steps.
+// Weight scales are read per lane, one byte per tile and step (staging them
+// in LDS as well measured no faster): in the row-major scale layout a wave's
+// 64 bytes of a step lie on 16 rows (lane offset 16-row stride, step stride 4),
+// in the packed layout of moe_pack_mx_scales they are contiguous in lane order
+// (lane offset = lane, step stride 64; one coalesced load, MXFP8 GEMM1 200 ->
+// 168 us on the MXFP8 layer).  The tokens' scales come from an LDS table the
+// workgroup fills per chunk of kTabSteps steps.
 template <int MT, int NT>
 struct MxAddr {
     const uint8_t* a[MT];    // weight tile bases (uniform)
     const uint8_t* as[MT];   // weight-scale tile bases (uniform)
     uint32_t aoff;           // lane offset into a weight tile, step 0
     uint32_t asoff;          // lane offset into a weight-scale tile, step 0
+    uint32_t asstep;         // its advance per K step (4 row-major, 64 packed)
     const uint8_t* b;        // token operand base (uniform)
     uint32_t boff[NT];       // lane offset of each token tile, step 0
     const uint8_t* bs[NT];   // the lane's byte in the LDS token-scale table, step 0
 };
+
+// Weight-scale lane offset and step stride for lane (lr, lk) = (row in the
+// 16-row tile, 32-element K block of the step); kb = scale bytes per row.
+template <int MT, int NT>
+__device__ __forceinline__ void set_scale_lane(MxAddr<MT, NT>& ad, const GemmArgs& g, int lr, int lk, int kb) {
+    ad.asoff = g.mx_packed ? uint32_t(lr + 16 * lk) : uint32_t(lr * kb + lk);
+    ad.asstep = g.mx_packed ? 64u : 4u;
+}
 
 template <bool kExact, int MT, int NT, int U>
 __device__ __forceinline__ void mx_load(MxStage<MT, NT, U>& st, const MxAddr<MT, NT>& ad, int step0) {
@@ -87,7 +100,7 @@ __device__ __forceinline__ void mx_load(MxStage<MT, NT, U>& st, const MxAddr<MT,
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             st.a[u][m] = ld32<kExact>(ad.a[m] + (ad.aoff + off));
-            st.sa[u][m] = ad.as[m][ad.asoff + 4 * (step0 + u)];
+            st.sa[u][m] = ad.as[m][ad.asoff + ad.asstep * uint32_t(step0 + u)];
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
@@ -174,7 +187,7 @@ __device__ __forceinline__ void mx_kloop(MxAddr<MT, NT> ad, RowScale row_scale, 
         }
         __syncthreads();
         ad.aoff = aoff0 + uint32_t(c0) * kStepK;
-        ad.asoff = asoff0 + 4 * c0;
+        ad.asoff = asoff0 + ad.asstep * uint32_t(c0);
 #pragma unroll
         for (int n = 0; n < NT; ++n) ad.boff[n] = boff0[n] + uint32_t(c0) * kStepK;
         mx_mainloop<kExact, MT, NT, 1>(ad, cs, acc);
@@ -212,7 +225,7 @@ __device__ __forceinline__ void gemm1_mx_tile(const GemmArgs& g, int blk, int ti
         ad.as[m] = w13s + row0 * kbh;
     }
     ad.aoff = uint32_t(lr * H + lk * 32);   // bf16 MFMA layout: the lane's MX block of the step
-    ad.asoff = uint32_t(lr * kbh + lk);
+    set_scale_lane(ad, g, lr, lk, kbh);
     ad.b = g.xq;
     const int32_t* rows = g.sorted_ids + blk * BM;
 #pragma unroll
@@ -317,7 +330,7 @@ __device__ __forceinline__ void gemm2_mx_tile(const GemmArgs& g, int blk, int ti
         ad.as[m] = w2s + row0 * kbi;
     }
     ad.aoff = uint32_t(lr * I + lk * 16);
-    ad.asoff = uint32_t(lr * kbi + lk);
+    set_scale_lane(ad, g, lr, lk, kbi);
     ad.b = static_cast<const uint8_t*>(g.inter) + int64_t(blk) * BM * I;
 #pragma unroll
     for (int n = 0; n < NT; ++n) ad.boff[n] = uint32_t((n * 16 + lr) * I + lk * 16);
@@ -379,7 +392,7 @@ __device__ __forceinline__ void gemm2_mx_tiles(const GemmArgs& g, int blk, int t
         ad.as[m] = w2s + row0 * kbi;
     }
     ad.aoff = uint32_t(lr * I + lk * 16);
-    ad.asoff = uint32_t(lr * kbi + lk);
+    set_scale_lane(ad, g, lr, lk, kbi);
     ad.b = static_cast<const uint8_t*>(g.inter) + int64_t(blk) * BM * I;
 
     // the block's token-scale table, all of K at once
@@ -412,7 +425,7 @@ __device__ __forceinline__ void gemm2_mx_tiles(const GemmArgs& g, int blk, int t
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             st.a[0][m] = ld32<false>(ad.a[m] + t * tile_bytes + (ad.aoff + off));
-            st.sa[0][m] = (ad.as[m] + t * tile_sbytes)[ad.asoff + 4 * k];
+            st.sa[0][m] = (ad.as[m] + t * tile_sbytes)[ad.asoff + ad.asstep * uint32_t(k)];
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {

@@ -76,6 +76,31 @@ hipError_t launch_gemm1_mx(const GemmArgs& g, hipStream_t s) {
     }
 }
 
+namespace {
+
+// Packed MXFP8 weight scales: output byte o is lane (o % 64) of K step
+// (o / 64) % (kb / 4) of 16-row group o / (16 kb); that lane's row and
+// 32-element block are (lane % 16, lane / 16) (kb = K / 32 bytes per row).
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ in, int64_t n, int kb,
+                                                             uint8_t* __restrict__ out) {
+    const int64_t o = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (o >= n) return;
+    const int64_t grp = o / (16 * kb);
+    const int rem = int(o - grp * 16 * kb);
+    const int step = rem >> 6, lane = rem & 63;
+    out[o] = in[(grp * 16 + (lane & 15)) * kb + 4 * step + (lane >> 4)];
+}
+
+}  // namespace
+
+hipError_t launch_pack_mx_scales(const uint8_t* scales, int E, int rows, int K, uint8_t* packed, hipStream_t s) {
+    const int kb = K / kMxBlock;
+    const int64_t n = int64_t(E) * rows * kb;
+    hipLaunchKernelGGL(pack_mx_scales_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, scales, n, kb,
+                       packed);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm2_mx(const GemmArgs& g, hipStream_t s) {
     switch (g.block_m) {
         case 16: return gemm2_mx<1>(g, s);

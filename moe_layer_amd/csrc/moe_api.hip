@@ -14,7 +14,8 @@ using namespace moe;
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 3;   // 1.1: MXFP8 weights; 1.2: layer variants; 1.3: moe_decode_layer
+constexpr int kVersionMinor = 4;   // 1.1: MXFP8 weights; 1.2: layer variants; 1.3: moe_decode_layer;
+                                   // 1.4: packed MXFP8 scales (moe_pack_mx_scales)
 // Rows per expert (on average) from which the LDS-tiled path beats weight
 // streaming.  Measured with bf16 weights (align + GEMM1 + GEMM2): E 128, H
 // 4096, I 1536 at 8 rows 0.90 ms streaming vs 1.08 tiled, 16 rows 1.14 vs 1.09,
@@ -51,7 +52,8 @@ int validate_forward_scalars(const moe_forward_args* a) {
     if (a->wdtype != MOE_WDTYPE_BF16 && a->wdtype != MOE_WDTYPE_FP8_E4M3 && a->wdtype != MOE_WDTYPE_MXFP8)
         return MOE_ERR_INVALID_ARG;
     if (a->path < MOE_PATH_AUTO || a->path > MOE_PATH_LARGE_M) return MOE_ERR_INVALID_ARG;
-    if ((a->flags & ~MOE_FLAG_WEIGHT_ON_INPUT) != 0) return MOE_ERR_INVALID_ARG;
+    if ((a->flags & ~(MOE_FLAG_WEIGHT_ON_INPUT | MOE_FLAG_MX_PACKED_SCALES)) != 0) return MOE_ERR_INVALID_ARG;
+    if ((a->flags & MOE_FLAG_MX_PACKED_SCALES) && a->wdtype != MOE_WDTYPE_MXFP8) return MOE_ERR_INVALID_ARG;
     if (!(a->clamp_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;   // negative or NaN
     if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 256)
         return MOE_ERR_UNSUPPORTED;
@@ -147,6 +149,7 @@ GemmArgs gemm_args(const moe_forward_args* a, const Plan& p, uint8_t* ws) {
     g.inter_scale = fp8 ? reinterpret_cast<float*>(ws + p.off_inter_scale) : nullptr;
     g.y = reinterpret_cast<float*>(ws + p.off_y);
     g.weight_on_input = (a->flags & MOE_FLAG_WEIGHT_ON_INPUT) != 0;
+    g.mx_packed = (a->flags & MOE_FLAG_MX_PACKED_SCALES) != 0;
     g.clamp = a->clamp_limit > 0.0f;
     g.clamp_limit = a->clamp_limit;
     return g;
@@ -220,6 +223,18 @@ MOE_API int moe_quant_act_mx(const void* x, int32_t rows, int32_t cols, uint8_t*
     if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
         return MOE_ERR_INVALID_ARG;
     return hip_status(launch_quant_act_mx(static_cast<const uint16_t*>(x), rows, cols, codes, scales, stream));
+}
+
+MOE_API int moe_pack_mx_scales(const uint8_t* scales, int32_t E, int32_t rows, int32_t K, uint8_t* packed,
+                               hipStream_t stream) {
+    if (E < 0 || rows < 0 || K < 0) return MOE_ERR_INVALID_ARG;
+    if (E < 1 || rows % 16 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    const int64_t bytes = int64_t(E) * rows * (K / MOE_MX_BLOCK);
+    if (bytes == 0) return MOE_OK;
+    if (!scales || !packed) return MOE_ERR_INVALID_ARG;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(scales), b0 = reinterpret_cast<uintptr_t>(packed);
+    if (a0 < b0 + uintptr_t(bytes) && b0 < a0 + uintptr_t(bytes)) return MOE_ERR_INVALID_ARG;   // overlap
+    return hip_status(launch_pack_mx_scales(scales, E, rows, K, packed, stream));
 }
 
 MOE_API int moe_plan(const moe_forward_args* a, moe_plan_info* out) {

@@ -19,12 +19,12 @@ _lib = None
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_WDTYPE_BF16, MOE_WDTYPE_FP8_E4M3, MOE_WDTYPE_MXFP8 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_SMALL_M, MOE_PATH_LARGE_M = 0, 1, 2
-MOE_FLAG_WEIGHT_ON_INPUT = 1
+MOE_FLAG_WEIGHT_ON_INPUT, MOE_FLAG_MX_PACKED_SCALES = 1, 2
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_QUANT_GROUP, MOE_MX_BLOCK = 1024, 64, 128, 32
 
 # every entry point include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_version", "moe_route", "moe_align_capacity", "moe_align",
-           "moe_quant_act", "moe_quant_act_mx", "moe_plan", "moe_forward_workspace", "moe_forward",
+           "moe_quant_act", "moe_quant_act_mx", "moe_pack_mx_scales", "moe_plan", "moe_forward_workspace", "moe_forward",
            "moe_forward_profiled", "moe_decode_layer")
 MOE_NUM_STAGES = 5
 MOE_SYNC_WORDS, MOE_SYNC_ERROR = 640, 576
@@ -77,6 +77,8 @@ def lib() -> C.CDLL:
         L.moe_quant_act.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_quant_act_mx.restype = C.c_int
         L.moe_quant_act_mx.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_pack_mx_scales.restype = C.c_int
+        L.moe_pack_mx_scales.argtypes = [vp, i32, i32, i32, vp, vp]
         L.moe_plan.restype = C.c_int
         L.moe_plan.argtypes = [C.POINTER(ForwardArgs), C.POINTER(PlanInfo)]
         L.moe_forward_workspace.restype = i64
@@ -172,6 +174,17 @@ def moe_quant_act_mx(x: torch.Tensor):
     return codes, scales
 
 
+def moe_pack_mx_scales(scales: torch.Tensor) -> torch.Tensor:
+    """The tile-packed copy of an MXFP8 weight's E8M0 scale bytes [E, rows, K/32]
+    (moe_pack_mx_scales; pass it with ``mx_packed_scales=True``)."""
+    assert scales.dtype == torch.uint8 and scales.is_contiguous() and scales.dim() == 3
+    E, rows, kb = scales.shape
+    packed = torch.empty_like(scales)
+    _check("moe_pack_mx_scales", lib().moe_pack_mx_scales(_ptr(scales), E, rows, kb * MOE_MX_BLOCK, _ptr(packed),
+                                                          _stream(scales.device)))
+    return packed
+
+
 def _u8(t):
     if t is None:
         return None
@@ -180,10 +193,11 @@ def _u8(t):
 
 def forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=None, out=None,
                  path=MOE_PATH_AUTO, block_m=0, shape=None, weight_on_input=False,
-                 clamp_limit=0.0) -> ForwardArgs:
+                 clamp_limit=0.0, mx_packed_scales=False) -> ForwardArgs:
     """Build the moe_forward_args struct.  With ``shape=(T, E, H, I, topk, wdtype)``
     the tensors may be None (for planning and validation).  ``weight_on_input``
-    and ``clamp_limit`` select the layer variants (0: no clamp)."""
+    and ``clamp_limit`` select the layer variants (0: no clamp);
+    ``mx_packed_scales`` says the MXFP8 scales come from moe_pack_mx_scales."""
     if shape is None:
         T, H = x.shape
         E, twoI, _ = w13.shape
@@ -200,7 +214,8 @@ def forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=No
     a.w2, a.w2_scale = _ptr(_u8(w2)), _ptr(w2_scale)
     a.topk_ids, a.topk_weights, a.out = _ptr(topk_ids), _ptr(topk_weights), _ptr(out)
     a.path, a.block_m = path, block_m
-    a.flags = MOE_FLAG_WEIGHT_ON_INPUT if weight_on_input else 0
+    a.flags = (MOE_FLAG_WEIGHT_ON_INPUT if weight_on_input else 0) | \
+        (MOE_FLAG_MX_PACKED_SCALES if mx_packed_scales else 0)
     a.clamp_limit = clamp_limit
     return a
 
@@ -219,10 +234,12 @@ def moe_forward_workspace(args: ForwardArgs) -> int:
 
 
 def moe_forward(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=None, out=None,
-                workspace=None, path=MOE_PATH_AUTO, block_m=0, weight_on_input=False, clamp_limit=0.0):
+                workspace=None, path=MOE_PATH_AUTO, block_m=0, weight_on_input=False, clamp_limit=0.0,
+                mx_packed_scales=False):
     """The fused MoE layer: bf16 x [T,H], w13 [E,2I,H], w2 [E,H,I] (bf16; or
     e4m3 with fp32 128x128 block scales; or e4m3 with E8M0 uint8 scales per row
-    and 32 K elements, MXFP8), int32 ids [T,k], fp32 weights [T,k].
+    and 32 K elements, MXFP8, row-major or, with ``mx_packed_scales``, from
+    moe_pack_mx_scales), int32 ids [T,k], fp32 weights [T,k].
     ``weight_on_input``: the router weight scales GEMM1's input row instead of
     GEMM2's output; ``clamp_limit`` > 0: SwiGLU clamp (gate <= L, |up| <= L).
     Returns (out bf16 [T,H], workspace)."""
@@ -230,7 +247,7 @@ def moe_forward(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=Non
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out, path, block_m,
-                     weight_on_input=weight_on_input, clamp_limit=clamp_limit)
+                     weight_on_input=weight_on_input, clamp_limit=clamp_limit, mx_packed_scales=mx_packed_scales)
     need = moe_forward_workspace(a)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
@@ -266,7 +283,7 @@ def decode_sync(device) -> torch.Tensor:
 
 def moe_decode_layer(x, w13, w2, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
                      router_logits=None, topk=None, renormalize=True, out=None, workspace=None, sync=None,
-                     weight_on_input=False, clamp_limit=0.0):
+                     weight_on_input=False, clamp_limit=0.0, mx_packed_scales=False):
     """The layer for few tokens as one kernel launch (the weight-streaming
     path with 16-row blocks).  With fp32 ``router_logits`` [T,E] it routes
     them (top ``topk``) into topk_ids / topk_weights (allocated when None);
@@ -280,7 +297,7 @@ def moe_decode_layer(x, w13, w2, topk_ids=None, topk_weights=None, w13_scale=Non
         topk_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
         topk_weights = torch.empty((T, topk), dtype=torch.float32, device=dev)
     a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out, MOE_PATH_SMALL_M, 16,
-                     weight_on_input=weight_on_input, clamp_limit=clamp_limit)
+                     weight_on_input=weight_on_input, clamp_limit=clamp_limit, mx_packed_scales=mx_packed_scales)
     need = moe_forward_workspace(a)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)

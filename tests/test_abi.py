@@ -154,7 +154,9 @@ def test_plan_large_path_limits():
     (dict(H=4032, wdtype=2, I=256), ops.MOE_ERR_UNSUPPORTED),   # MXFP8 needs H % 128 == 0
     (dict(wdtype=3), ops.MOE_ERR_INVALID_ARG),
     (dict(T=1 << 20, H=4096, I=256, wdtype=2), ops.MOE_ERR_UNSUPPORTED),   # MXFP8: T * H < 2^32
-    (dict(flags=2), ops.MOE_ERR_INVALID_ARG),               # unknown flag bit
+    (dict(flags=4), ops.MOE_ERR_INVALID_ARG),               # unknown flag bit
+    (dict(flags=ops.MOE_FLAG_MX_PACKED_SCALES), ops.MOE_ERR_INVALID_ARG),               # packed scales: MXFP8 only
+    (dict(flags=ops.MOE_FLAG_MX_PACKED_SCALES, wdtype=1, I=256), ops.MOE_ERR_INVALID_ARG),
     (dict(flags=-1), ops.MOE_ERR_INVALID_ARG),
     (dict(clamp_limit=-1.0), ops.MOE_ERR_INVALID_ARG),
     (dict(clamp_limit=float("nan")), ops.MOE_ERR_INVALID_ARG),
@@ -173,6 +175,27 @@ def test_forward_variants_plan_like_the_plain_layer():
         p = ops.moe_plan(_args(**kw))
         ref = base if "wdtype" not in kw else ops.moe_plan(_args(wdtype=1, I=256))
         assert p == ref
+
+
+def test_mx_packed_scales_plan_like_row_major():
+    """The packed MXFP8 scale layout changes only where the kernels read the
+    scale bytes: same plan, same workspace."""
+    assert ops.moe_plan(_args(wdtype=2, I=256, flags=ops.MOE_FLAG_MX_PACKED_SCALES)) == \
+        ops.moe_plan(_args(wdtype=2, I=256))
+
+
+def test_pack_mx_scales_validation():
+    L = ops.lib()
+    f, g = C.c_void_p(FAKE), C.c_void_p(FAKE + (1 << 30))
+    assert L.moe_pack_mx_scales(f, 2, 20, 128, g, None) == ops.MOE_ERR_UNSUPPORTED    # rows % 16
+    assert L.moe_pack_mx_scales(f, 2, 16, 96, g, None) == ops.MOE_ERR_UNSUPPORTED     # K % 128
+    assert L.moe_pack_mx_scales(f, 0, 16, 128, g, None) == ops.MOE_ERR_UNSUPPORTED    # no experts
+    assert L.moe_pack_mx_scales(f, -1, 16, 128, g, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_mx_scales(f, 2, -16, 128, g, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_mx_scales(None, 2, 16, 128, g, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_mx_scales(f, 2, 16, 128, None, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_mx_scales(f, 2, 16, 128, C.c_void_p(FAKE + 64), None) == ops.MOE_ERR_INVALID_ARG  # overlap
+    assert L.moe_pack_mx_scales(None, 2, 0, 128, None, None) == ops.MOE_OK             # nothing to pack
 
 
 def test_forward_workspace_errors():

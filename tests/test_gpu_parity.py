@@ -373,6 +373,39 @@ def test_block_m_invariance_bitwise(name, wdtype):
             assert torch.equal(out, ref), f"block_m={bm}"
 
 
+def test_pack_mx_scales_layout():
+    """moe_pack_mx_scales against its definition written as a numpy reshape:
+    packed[((e*rows/16 + t)*K/128 + s)*64 + g*16 + r] = scales[e, 16t + r, 4s + g]."""
+    rng = np.random.default_rng(9)
+    for E, rows, K in [(1, 16, 128), (3, 48, 384), (2, 512, 4096)]:
+        sc = rng.integers(0, 256, size=(E, rows, K // 32), dtype=np.uint8)
+        want = sc.reshape(E, rows // 16, 16, K // 128, 4).transpose(0, 1, 3, 4, 2).reshape(E, rows, K // 32)
+        got = ops.moe_pack_mx_scales(torch.from_numpy(sc).to(dev()))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("name,block_m", [("tiny", 16), ("tiny", 32), ("tiny", 64), ("mxfp8", 0)])
+def test_mx_packed_scales_bitwise(name, block_m):
+    """The MXFP8 layer with its weight scales in the packed layout gives the
+    same bits as with the row-major scales (same values, same arithmetic)."""
+    cfg = replace(CONFIGS[name], wdtype="mxfp8")
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    ref, _, (x, ids_t, tw_t) = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=block_m)
+    s13p, s2p = ops.moe_pack_mx_scales(layer.s13), ops.moe_pack_mx_scales(layer.s2)
+    out, _ = ops.moe_forward(x, layer.w13, layer.w2, ids_t, tw_t, s13p, s2p, block_m=block_m,
+                             mx_packed_scales=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    if name == "tiny":   # the single-launch layer reads the packed scales too
+        sync = torch.zeros(ops.MOE_SYNC_WORDS, dtype=torch.int32, device=dev())
+        ref16, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_SMALL_M, block_m=16)
+        dl, _, _, _ = ops.moe_decode_layer(x, layer.w13, layer.w2, ids_t, tw_t, s13p, s2p, sync=sync,
+                                           mx_packed_scales=True)
+        torch.cuda.synchronize()
+        assert torch.equal(dl, ref16)
+
+
 @pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp8"])
 def test_token_permutation_equivariance(name):
     cfg = CONFIGS[name]
