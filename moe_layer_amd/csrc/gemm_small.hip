@@ -83,8 +83,6 @@ hipError_t gemm2_bf16(const GemmArgs& g, hipStream_t s) {
 // Column tiles per workgroup, measured on the fp8 layer (1024 tokens, 256
 // experts, H 4096, I 256): GEMM2 113 (one tile) / 101.5 (2) / 109 (4) / 110
 // (8) / 137 us (16) at 32-token blocks; 145 / 130 / 121 / 126 / 125 us at 64.
-// 32 output rows per wave with 4 tiles (the same 512 rows per workgroup,
-// 4 instead of 3 workgroups per CU) ran 121 against 102 us.
 template <int NT, int WT>
 hipError_t gemm2_fp8(const GemmArgs& g, hipStream_t s) {
     constexpr int NW = 4, kTiles = NT >= 4 ? 4 : 2;
