@@ -241,12 +241,15 @@ def test_forward_ragged_large_path():
     assert excess <= TAU["bf16"]
 
 
-def test_forward_large_path_short_tail_blocks():
+@pytest.mark.parametrize("variant", ["plain", "on_input", "clamp"])
+def test_forward_large_path_short_tail_blocks(variant):
     """The LDS-tiled path where an expert's last 256-row block holds 1, 32, 33
     or 64 rows (taken by the workgroup of the expert's previous block as token
     rows 256..319), 65 rows (a block of its own), a three-block expert whose
     third block is short, an expert of exactly one full block and a small one;
-    every token compared with the oracle."""
+    every token compared with the oracle, for the plain layer and the layer
+    variants (their epilogues run on the taken rows too)."""
+    kw = {} if variant == "plain" else _VARIANTS[variant]
     from moe_layer_amd.workloads import Config
     counts = [257, 288, 289, 320, 321, 576, 256, 5]
     k = 2
@@ -262,11 +265,12 @@ def test_forward_large_path_short_tail_blocks():
     plan = ops.moe_plan(ops.forward_args(None, None, None, None, None, path=ops.MOE_PATH_LARGE_M,
                                          shape=(T, len(counts), 512, 384, k, 0)))
     assert plan["block_m"] == 256
-    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_LARGE_M)
+    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_LARGE_M, **kw)
     gpu = out.to(torch.float64).cpu().numpy()
-    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(T))
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(T),
+                      kw.get("weight_on_input", False), kw.get("clamp_limit", 0.0))
     excess, raw, _ = compare_output(gpu, o)
-    log(f"short tails: excess/RMS={excess:.3e} raw={raw:.3e}")
+    log(f"short tails {variant}: excess/RMS={excess:.3e} raw={raw:.3e}")
     assert np.all(np.isfinite(gpu))
     assert excess <= TAU["bf16"]
 
@@ -385,23 +389,25 @@ def test_pack_mx_scales_layout():
         np.testing.assert_array_equal(got.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("name,block_m", [("tiny", 16), ("tiny", 32), ("tiny", 64), ("mxfp8", 0)])
-def test_mx_packed_scales_bitwise(name, block_m):
+@pytest.mark.parametrize("name,block_m,variant", [("tiny", 16, "plain"), ("tiny", 32, "plain"), ("tiny", 64, "plain"),
+                                                  ("tiny", 16, "both"), ("mxfp8", 0, "plain"), ("mxfp8", 0, "clamp")])
+def test_mx_packed_scales_bitwise(name, block_m, variant):
     """The MXFP8 layer with its weight scales in the packed layout gives the
     same bits as with the row-major scales (same values, same arithmetic)."""
+    kw = {} if variant == "plain" else _VARIANTS[variant]
     cfg = replace(CONFIGS[name], wdtype="mxfp8")
     wl, layer, ids, tw = _layer_inputs(cfg)
-    ref, _, (x, ids_t, tw_t) = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=block_m)
+    ref, _, (x, ids_t, tw_t) = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=block_m, **kw)
     s13p, s2p = ops.moe_pack_mx_scales(layer.s13), ops.moe_pack_mx_scales(layer.s2)
     out, _ = ops.moe_forward(x, layer.w13, layer.w2, ids_t, tw_t, s13p, s2p, block_m=block_m,
-                             mx_packed_scales=True)
+                             mx_packed_scales=True, **kw)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     if name == "tiny":   # the single-launch layer reads the packed scales too
         sync = torch.zeros(ops.MOE_SYNC_WORDS, dtype=torch.int32, device=dev())
-        ref16, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_SMALL_M, block_m=16)
+        ref16, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_SMALL_M, block_m=16, **kw)
         dl, _, _, _ = ops.moe_decode_layer(x, layer.w13, layer.w2, ids_t, tw_t, s13p, s2p, sync=sync,
-                                           mx_packed_scales=True)
+                                           mx_packed_scales=True, **kw)
         torch.cuda.synchronize()
         assert torch.equal(dl, ref16)
 
