@@ -186,9 +186,24 @@ struct GemmArgs {
     float* y;                   // fp32 [T*topk, H]
     int weight_on_input;        // router weight on GEMM1's input instead of GEMM2's output
     int mx_packed;              // MXFP8 weight scales in the tile-packed layout (moe_pack_mx_scales)
+    int krot;                   // GEMM1 walks K from a per-(expert, column tile) start (k_rotation)
     int clamp;                  // SwiGLU clamp on (limit clamp_limit)
     float clamp_limit;
 };
+
+// First K step of the fp8 and MXFP8 GEMM1 for expert e's column tile (the
+// walk wraps around).  With every workgroup starting at step 0, the whole
+// chip reads the same byte offset of its weight rows at the same time;
+// starting the experts' tiles at spread-out steps measured 25-35 % faster
+// fp8 / MXFP8 GEMM1s where experts hold about one block each (64 and 256
+// tokens of the fp8 layer: 127 -> 94 and 154 -> 109 us; MXFP8 at 256 tokens
+// 166 -> 110 us).  The planner turns it on up to 16 routed rows per expert
+// (GemmArgs::krot); the bf16 decode GEMM1 ran slower with it (355 -> 402 us)
+// and does not use it.  It depends on (e, tile) only, so a product's K order
+// is the same for every block size and both launch forms.
+__device__ __forceinline__ int k_rotation(const GemmArgs& g, int e, int tile, int nsteps) {
+    return g.krot ? (e * 37 + tile * 11) % nsteps : 0;
+}
 
 // Router weight a GEMM1 epilogue applies to sorted slot f (1 unless the
 // weight goes on the input; 0 for padding rows, which are never stored as

@@ -93,19 +93,22 @@ __device__ __forceinline__ void set_scale_lane(MxAddr<MT, NT>& ad, const GemmArg
 }
 
 template <bool kExact, int MT, int NT, int U>
-__device__ __forceinline__ void mx_load(MxStage<MT, NT, U>& st, const MxAddr<MT, NT>& ad, int step0) {
+__device__ __forceinline__ void mx_load(MxStage<MT, NT, U>& st, const MxAddr<MT, NT>& ad, int step0, int rot = 0,
+                                        int nst = 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t off = uint32_t(step0 + u) * kStepK;
+        int sidx = step0 + u + rot;   // the walk's step step0 + u is K step (step0 + u + rot) mod nst (k_rotation)
+        if (sidx >= nst && rot) sidx -= nst;
+        const uint32_t off = uint32_t(sidx) * kStepK;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             st.a[u][m] = ld32<kExact>(ad.a[m] + (ad.aoff + off));
-            st.sa[u][m] = ad.as[m][ad.asoff + ad.asstep * uint32_t(step0 + u)];
+            st.sa[u][m] = ad.as[m][ad.asoff + ad.asstep * uint32_t(sidx)];
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             st.b[u][n] = ld32<kExact>(ad.b + (ad.boff[n] + off));
-            st.sb[u][n] = ad.bs[n][4 * (step0 + u)];
+            st.sb[u][n] = ad.bs[n][4 * sidx];
         }
     }
 }
@@ -151,14 +154,14 @@ __device__ __forceinline__ void mx_compute(const MxStage<MT, NT, U>& st, f32x4 (
 
 // K loop over nsteps steps, two register stages (the block-fp8 kernels' loop).
 template <bool kExact, int MT, int NT, int U>
-__device__ __forceinline__ void mx_mainloop(const MxAddr<MT, NT>& ad, int nsteps, f32x4 (&acc)[MT][NT]) {
+__device__ __forceinline__ void mx_mainloop(const MxAddr<MT, NT>& ad, int nsteps, f32x4 (&acc)[MT][NT], int rot = 0) {
     MxStage<MT, NT, U> s0, s1;
-    mx_load<kExact, MT, NT, U>(s0, ad, 0);
+    mx_load<kExact, MT, NT, U>(s0, ad, 0, rot, nsteps);
     for (int k = 0; k < nsteps; k += 2 * U) {
         const bool has1 = k + U < nsteps;
-        if (has1) mx_load<kExact, MT, NT, U>(s1, ad, k + U);
+        if (has1) mx_load<kExact, MT, NT, U>(s1, ad, k + U, rot, nsteps);
         mx_compute<kExact, MT, NT, U>(s0, acc);
-        if (k + 2 * U < nsteps) mx_load<kExact, MT, NT, U>(s0, ad, k + 2 * U);
+        if (k + 2 * U < nsteps) mx_load<kExact, MT, NT, U>(s0, ad, k + 2 * U, rot, nsteps);
         if (has1) mx_compute<kExact, MT, NT, U>(s1, acc);
     }
 }
@@ -167,7 +170,8 @@ __device__ __forceinline__ void mx_mainloop(const MxAddr<MT, NT>& ad, int nsteps
 // (row_scale(r) points at row r's first byte) in LDS, then run the K loop.
 template <bool kExact, int MT, int NT, int BM, int NTHREADS, typename RowScale>
 __device__ __forceinline__ void mx_kloop(MxAddr<MT, NT> ad, RowScale row_scale, int nsteps, uint8_t* tab,
-                                         f32x4 (&acc)[MT][NT]) {
+                                         f32x4 (&acc)[MT][NT], int rot = 0) {
+    if (nsteps > kTabSteps) rot = 0;   // the rotated walk stays inside one table chunk
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15, lk = lane >> 4;
     const uint32_t aoff0 = ad.aoff, asoff0 = ad.asoff;
@@ -190,7 +194,7 @@ __device__ __forceinline__ void mx_kloop(MxAddr<MT, NT> ad, RowScale row_scale, 
         ad.asoff = asoff0 + ad.asstep * uint32_t(c0);
 #pragma unroll
         for (int n = 0; n < NT; ++n) ad.boff[n] = boff0[n] + uint32_t(c0) * kStepK;
-        mx_mainloop<kExact, MT, NT, 1>(ad, cs, acc);
+        mx_mainloop<kExact, MT, NT, 1>(ad, cs, acc, rot);
     }
 }
 
@@ -246,7 +250,7 @@ __device__ __forceinline__ void gemm1_mx_tile(const GemmArgs& g, int blk, int ti
         const int f = rows[r];
         return xs + int64_t(f < R ? f / g.topk : 0) * kbh;
     };
-    mx_kloop<true, MT, NT, BM, NW * 64>(ad, row_scale, H / kStepK, tab, acc);
+    mx_kloop<true, MT, NT, BM, NW * 64>(ad, row_scale, H / kStepK, tab, acc, k_rotation(g, e, tile, H / kStepK));
 
     // epilogue: a = silu(g) * u with the bf16 rounding points
     float a[WT][NT][4];

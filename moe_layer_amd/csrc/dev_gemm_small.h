@@ -90,11 +90,13 @@ template <bool FP8, int MT, int NT, int U>
 __device__ __forceinline__ void load_stage(Stage<FP8, MT, NT, U>& st, const uint8_t* const (&ap)[MT],
                                            const uint8_t* const (&bp)[NT],
                                            const float* const (&asp)[MT],
-                                           const float* const (&bsp)[NT], int step0) {
+                                           const float* const (&bsp)[NT], int step0, int rot = 0, int nst = 0) {
     using O = Op<FP8>;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t off = int64_t(step0 + u) * O::kStepBytes;
+        int sidx = step0 + u + rot;   // the walk's step step0 + u is K step (step0 + u + rot) mod nst
+        if (sidx >= nst && rot) sidx -= nst;
+        const int64_t off = int64_t(sidx) * O::kStepBytes;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -105,9 +107,9 @@ __device__ __forceinline__ void load_stage(Stage<FP8, MT, NT, U>& st, const uint
             for (int p = 0; p < O::kParts; ++p) st.b[u][n][p] = ld16(bp[n] + off + 16 * p);
         if constexpr (FP8) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m) st.sa[u][m] = ld_uniform(asp[m] + step0 + u);   // weight block
+            for (int m = 0; m < MT; ++m) st.sa[u][m] = ld_uniform(asp[m] + sidx);   // weight block
 #pragma unroll
-            for (int n = 0; n < NT; ++n) st.sb[u][n] = bsp[n][step0 + u];                // LDS table
+            for (int n = 0; n < NT; ++n) st.sb[u][n] = bsp[n][sidx];                // LDS table
         }
     }
 }
@@ -200,14 +202,14 @@ __device__ __forceinline__ void compute_stage(const Stage<FP8, MT, NT, U>& st, f
 template <bool FP8, bool kExact, int MT, int NT, int U>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&ap)[MT], const uint8_t* const (&bp)[NT],
                                          const float* const (&asp)[MT], const float* const (&bsp)[NT],
-                                         int nsteps, f32x4 (&acc)[MT][NT]) {
+                                         int nsteps, f32x4 (&acc)[MT][NT], int rot = 0) {
     Stage<FP8, MT, NT, U> s0, s1;
-    load_stage<FP8, MT, NT, U>(s0, ap, bp, asp, bsp, 0);
+    load_stage<FP8, MT, NT, U>(s0, ap, bp, asp, bsp, 0, rot, nsteps);
     for (int k = 0; k < nsteps; k += 2 * U) {
         const bool has1 = k + U < nsteps;
-        if (has1) load_stage<FP8, MT, NT, U>(s1, ap, bp, asp, bsp, k + U);
+        if (has1) load_stage<FP8, MT, NT, U>(s1, ap, bp, asp, bsp, k + U, rot, nsteps);
         compute_stage<FP8, kExact, MT, NT, U>(s0, acc);
-        if (k + 2 * U < nsteps) load_stage<FP8, MT, NT, U>(s0, ap, bp, asp, bsp, k + 2 * U);
+        if (k + 2 * U < nsteps) load_stage<FP8, MT, NT, U>(s0, ap, bp, asp, bsp, k + 2 * U, rot, nsteps);
         if (has1) compute_stage<FP8, kExact, MT, NT, U>(s1, acc);
     }
 }
@@ -218,8 +220,9 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&ap)[MT], const u
 template <bool kExact, int MT, int NT, int BM, int NTHREADS, typename RowScale>
 __device__ __forceinline__ void mainloop_fp8(const uint8_t* const (&ap)[MT], const uint8_t* const (&bp)[NT],
                                              const float* const (&asp)[MT], RowScale row_scale, int nsteps,
-                                             float* tab, f32x4 (&acc)[MT][NT]) {
+                                             float* tab, f32x4 (&acc)[MT][NT], int rot = 0) {
     using O = Op<true>;
+    if (nsteps > kTabSteps) rot = 0;   // the rotated walk stays inside one table chunk
     const int lr = threadIdx.x & 15;
     for (int c0 = 0; c0 < nsteps; c0 += kTabSteps) {
         const int cs = min(kTabSteps, nsteps - c0);
@@ -243,7 +246,7 @@ __device__ __forceinline__ void mainloop_fp8(const uint8_t* const (&ap)[MT], con
             bpc[n] = bp[n] + int64_t(c0) * O::kStepBytes;
             bspc[n] = tab + (n * 16 + lr) * kTabStride;
         }
-        mainloop<true, kExact, MT, NT, 1>(apc, bpc, aspc, bspc, cs, acc);
+        mainloop<true, kExact, MT, NT, 1>(apc, bpc, aspc, bspc, cs, acc, rot);
     }
 }
 
@@ -252,7 +255,9 @@ __device__ __forceinline__ void mainloop_fp8(const uint8_t* const (&ap)[MT], con
 //   WT gate tiles and WT up tiles (16 rows each) per wave; NW waves per block
 //   cover NW*WT*16 intermediate columns; BM = 16*NT tokens.
 // ----------------------------------------------------------------------------
-template <bool FP8, int NT, int WT, int NW, int U>
+// kRot (fp8 only): walk K from k_rotation's start; the caller picks the
+// instance from GemmArgs::krot, so the unrotated one keeps its plain loop.
+template <bool FP8, int NT, int WT, int NW, int U, bool kRot = false>
 __device__ __forceinline__ void gemm1_small_tile(const GemmArgs& g, int blk, int tile) {
     using O = Op<FP8>;
     constexpr int MT = 2 * WT;
@@ -301,7 +306,9 @@ __device__ __forceinline__ void gemm1_small_tile(const GemmArgs& g, int blk, int
             const int f = rows[r];
             return g.xs + int64_t(f < R ? f / g.topk : 0) * kb_count;
         };
-        mainloop_fp8<true, MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, H / O::kStepK, tab, acc);
+        const int nst = H / O::kStepK;
+        mainloop_fp8<true, MT, NT, BM, NW * 64>(ap, bp, asp, row_scale, nst, tab, acc,
+                                                kRot ? k_rotation(g, e, tile, nst) : 0);
     } else {
         mainloop<FP8, false, MT, NT, U>(ap, bp, asp, bsp, H / O::kStepK, acc);
     }

@@ -183,7 +183,10 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(FusedArgs a) {
     for_items(int64_t(active) * a.ntiles1, wg, nwg, [&](int64_t item) {
         const int tile = int(item / active), blk = int(item - int64_t(tile) * active);
         if constexpr (W == 0) small_gemm::gemm1_small_tile<false, 1, 1, 4, 4>(g, blk, tile);
-        else if constexpr (W == 1) small_gemm::gemm1_small_tile<true, 1, 2, 4, 1>(g, blk, tile);
+        else if constexpr (W == 1) {
+            if (g.krot) small_gemm::gemm1_small_tile<true, 1, 2, 4, 1, true>(g, blk, tile);
+            else small_gemm::gemm1_small_tile<true, 1, 2, 4, 1>(g, blk, tile);
+        }
         else mx_gemm::gemm1_mx_tile<1, 2, 4>(g, blk, tile);
     });
     grid_barrier(a.sync, ++bar, nwg);

@@ -9,11 +9,13 @@ namespace {
 
 using namespace small_gemm;
 
-template <bool FP8, int NT, int WT, int NW, int U>
+// kRot: the fp8 GEMM1 with the rotated K walk (a separate kernel, so the
+// plain one keeps its own code and registers; the host picks by g.krot)
+template <bool FP8, int NT, int WT, int NW, int U, bool kRot = false>
 __global__ __launch_bounds__(NW * 64) void gemm1_small_kernel(GemmArgs g, int ntiles) {
     int blk, tile;
     if (!map_active_tile(g, ntiles, blk, tile)) return;
-    gemm1_small_tile<FP8, NT, WT, NW, U>(g, blk, tile);
+    gemm1_small_tile<FP8, NT, WT, NW, U, kRot>(g, blk, tile);
 }
 
 // GEMM2 takes its items block-major: the column tiles of one expert block,
@@ -50,8 +52,12 @@ hipError_t gemm1_dispatch(const GemmArgs& g, hipStream_t s) {
         // one 128-column group per workgroup: 4 waves x (32 gate + 32 up)
         // rows, or 8 waves x (16 + 16) for 64-token blocks (registers)
         const int ntiles = g.I / 128;
-        if constexpr (NT <= 2) return launch_tiles(gemm1_small_kernel<true, NT, 2, 4, 1>, g, ntiles, 256, s);
-        else return launch_tiles(gemm1_small_kernel<true, NT, 1, 8, 1>, g, ntiles, 512, s);
+        if constexpr (NT <= 2)
+            return g.krot ? launch_tiles(gemm1_small_kernel<true, NT, 2, 4, 1, true>, g, ntiles, 256, s)
+                          : launch_tiles(gemm1_small_kernel<true, NT, 2, 4, 1>, g, ntiles, 256, s);
+        else
+            return g.krot ? launch_tiles(gemm1_small_kernel<true, NT, 1, 8, 1, true>, g, ntiles, 512, s)
+                          : launch_tiles(gemm1_small_kernel<true, NT, 1, 8, 1>, g, ntiles, 512, s);
     } else {
         // 4 waves x (16 gate + 16 up) = 64 columns.  16-row blocks take 8
         // K-steps per register stage (twice the bytes in flight per wave at
