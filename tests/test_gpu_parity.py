@@ -377,6 +377,24 @@ def test_block_m_invariance_bitwise(name, wdtype):
             assert torch.equal(out, ref), f"block_m={bm}"
 
 
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
+def test_rotated_k_walk_parity_and_block_m_invariance(wdtype):
+    """64 tokens of the fp8 / MXFP8 layer (2 routed rows per expert: GEMM1's
+    rotated K walk is on, 32 K-steps): oracle parity, and the same bits for
+    block sizes 16, 32 and 64 (the walk's start depends on the expert and the
+    column tile only)."""
+    cfg = CONFIGS[wdtype].with_tokens(64)
+    _forward_case(cfg, tokens=np.arange(0, 64, 3))
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    ref = None
+    for bm in (16, 32, 64):
+        out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=bm)
+        if ref is None:
+            ref = out.clone()
+        else:
+            assert torch.equal(out, ref), f"block_m={bm}"
+
+
 def test_pack_mx_scales_layout():
     """moe_pack_mx_scales against its definition written as a numpy reshape:
     packed[((e*rows/16 + t)*K/128 + s)*64 + g*16 + r] = scales[e, 16t + r, 4s + g]."""
