@@ -186,7 +186,7 @@ struct GemmArgs {
     float* y;                   // fp32 [T*topk, H]
     int weight_on_input;        // router weight on GEMM1's input instead of GEMM2's output
     int mx_packed;              // MXFP8 weight scales in the tile-packed layout (moe_pack_mx_scales)
-    int krot;                   // GEMM1 walks K from a per-(expert, column tile) start (k_rotation)
+    int krot;                   // the fp8 GEMM1 walks K from a per-(expert, column tile) start (k_rotation)
     int clamp;                  // SwiGLU clamp on (limit clamp_limit)
     float clamp_limit;
 };
@@ -197,12 +197,15 @@ struct GemmArgs {
 // starting the experts' tiles at spread-out steps measured 25-35 % faster
 // fp8 / MXFP8 GEMM1s where experts hold about one block each (64 and 256
 // tokens of the fp8 layer: 127 -> 94 and 154 -> 109 us; MXFP8 at 256 tokens
-// 166 -> 110 us).  The planner turns it on up to 16 routed rows per expert
-// (GemmArgs::krot); the bf16 decode GEMM1 ran slower with it (355 -> 402 us)
-// and does not use it.  It depends on (e, tile) only, so a product's K order
-// is the same for every block size and both launch forms.
+// 166 -> 110 us).  The MXFP8 GEMM1 always starts there (also faster at 1024
+// and 2048 tokens: 171 -> 163 and 307 -> 302 us); the fp8 one only up to 16
+// routed rows per expert (GemmArgs::krot: at 1024 tokens 164 -> 172 us); the
+// bf16 decode GEMM1 ran slower with it (355 -> 402 us) and does not use it.
+// It depends on (e, tile) only, so a product's K order is the same for every
+// block size and both launch forms.
+__device__ __forceinline__ int k_rotation_start(int e, int tile, int nsteps) { return (e * 37 + tile * 11) % nsteps; }
 __device__ __forceinline__ int k_rotation(const GemmArgs& g, int e, int tile, int nsteps) {
-    return g.krot ? (e * 37 + tile * 11) % nsteps : 0;
+    return g.krot ? k_rotation_start(e, tile, nsteps) : 0;
 }
 
 // Router weight a GEMM1 epilogue applies to sorted slot f (1 unless the

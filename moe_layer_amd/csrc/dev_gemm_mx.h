@@ -250,7 +250,7 @@ __device__ __forceinline__ void gemm1_mx_tile(const GemmArgs& g, int blk, int ti
         const int f = rows[r];
         return xs + int64_t(f < R ? f / g.topk : 0) * kbh;
     };
-    mx_kloop<true, MT, NT, BM, NW * 64>(ad, row_scale, H / kStepK, tab, acc, k_rotation(g, e, tile, H / kStepK));
+    mx_kloop<true, MT, NT, BM, NW * 64>(ad, row_scale, H / kStepK, tab, acc, k_rotation_start(e, tile, H / kStepK));
 
     // epilogue: a = silu(g) * u with the bf16 rounding points
     float a[WT][NT][4];

@@ -30,9 +30,9 @@ constexpr int64_t kLargeMinGemm1Tiles = 256;
 // From this many routed slots on, the alignment runs on many workgroups (one
 // workgroup's ALUs bound it above a few thousand slots).
 constexpr int64_t kAlignWideMinSlots = 2048;
-// The fp8 / MXFP8 GEMM1 walks K from a per-(expert, tile) start up to this
-// many routed rows per expert (k_rotation; fp8 layer: 64 tokens 127 -> 94 us,
-// 256 tokens 154 -> 109 us, 512 tokens 143 -> 138 us).
+// The fp8 GEMM1 walks K from a per-(expert, tile) start up to this many
+// routed rows per expert (k_rotation; fp8 layer: 64 tokens 127 -> 94 us, 256
+// tokens 154 -> 109 us, 512 tokens 143 -> 138 us; the MXFP8 GEMM1 always does).
 constexpr int64_t kRotateMaxRowsPerExpert = 16;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -154,7 +154,7 @@ GemmArgs gemm_args(const moe_forward_args* a, const Plan& p, uint8_t* ws) {
     g.y = reinterpret_cast<float*>(ws + p.off_y);
     g.weight_on_input = (a->flags & MOE_FLAG_WEIGHT_ON_INPUT) != 0;
     g.mx_packed = (a->flags & MOE_FLAG_MX_PACKED_SCALES) != 0;
-    // the fp8 / MXFP8 GEMM1's rotated K walk: on while experts hold about one block each
+    // the fp8 GEMM1's rotated K walk: on while experts hold about one block each
     g.krot = int64_t(a->T) * a->topk <= kRotateMaxRowsPerExpert * int64_t(a->E);
     g.clamp = a->clamp_limit > 0.0f;
     g.clamp_limit = a->clamp_limit;
