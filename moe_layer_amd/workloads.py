@@ -249,3 +249,70 @@ class Workload:
                 else:
                     fn(e, w)
         return out
+
+
+# ----------------------------------------------------------------------------
+# Exact-sum layers: inputs on which every partial sum of the gate/up GEMM is
+# an exact fp32 value, whatever order the products are added in, so the
+# rounding points after it (bf16 gate/up, SiLU, product, fp8 codes) have one
+# correct result that a test can demand bit for bit.
+# ----------------------------------------------------------------------------
+
+def _e4m3_bytes(v: np.ndarray) -> np.ndarray:
+    """Values already on the E4M3FN grid -> their bytes (torch's CPU cast)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def exact_sum_layer(T: int, E: int, H: int, I: int, topk: int, wdtype: str, seed: int = 0,
+                    pow2_route_weights: bool = False, hot_expert: int | None = None):
+    """A seeded layer whose activations are i/8 with i uniform in [-7, 7] and
+    whose weights are j/32 with j uniform in [-3, 3] (bf16), or e4m3 codes of
+    j/2 times a power-of-two block scale drawn from {2^-3, 2^-4, 2^-5} (fp8:
+    per 128x128 block; MXFP8: an E8M0 byte per row and 32 K elements).  Every
+    product is a small integer times 2^-11 or coarser and |sum| < 2^24 of those
+    units for H < 2^16, so fp32 accumulation is exact in any order; x also
+    survives the fp8 activation quantisation unchanged (at most 3 significant
+    bits, scaled by a power of two).
+
+    Routing: ids uniform over [0, E) with duplicates, plus one unrouted slot
+    (id -1) and one id E when T * topk > 4; ``hot_expert`` takes a third of
+    the tokens' first slot.  Weights: softmax of N(0, 1) in fp32, or powers
+    of two from {1, 1/2, 1/4} with ``pow2_route_weights`` (scaling h by them
+    is exact).  Returns dict(x_bits uint16 [T,H], ids int32 [T,k], tw fp32
+    [T,k], experts: list of layer-format (w13, s13, w2, s2) per expert, as
+    Workload.expert_weights gives them)."""
+    from scipy.special import softmax
+    g = np.random.default_rng([seed, 100 + TID_X])
+    x = g.integers(-7, 8, size=(T, H)).astype(np.float32) / np.float32(8.0)
+    gi = np.random.default_rng([seed, 100 + TID_IDS])
+    ids = gi.integers(0, E, size=(T, topk)).astype(np.int32)
+    if hot_expert is not None:
+        ids[: T // 3, 0] = hot_expert
+    if T * topk > 4:
+        ids[0, topk - 1] = -1
+        ids[min(1, T - 1), 0] = E
+    gt = np.random.default_rng([seed, 100 + TID_TW])
+    if pow2_route_weights:
+        tw = np.ldexp(1.0, -gt.integers(0, 3, size=(T, topk))).astype(np.float32)
+    else:
+        tw = softmax(gt.standard_normal((T, topk)), axis=1).astype(np.float32)
+    experts = []
+    for e in range(E):
+        ge = np.random.default_rng([seed, 100 + TID_W13, e])
+        w13i = ge.integers(-3, 4, size=(2 * I, H)).astype(np.float32)
+        w2i = ge.integers(-3, 4, size=(H, I)).astype(np.float32)
+        if wdtype == "bf16":
+            experts.append((to_bf16_bits(w13i / 32), None, to_bf16_bits(w2i / 32), None))
+        elif wdtype == "fp8":
+            s13 = np.ldexp(1.0, -ge.integers(3, 6, size=(2 * I // 128, H // 128))).astype(np.float32)
+            s2 = np.ldexp(1.0, -ge.integers(3, 6, size=(H // 128, I // 128))).astype(np.float32)
+            experts.append((_e4m3_bytes(w13i / 2), s13, _e4m3_bytes(w2i / 2), s2))
+        elif wdtype == "mxfp8":
+            s13 = (127 - ge.integers(3, 6, size=(2 * I, H // 32))).astype(np.uint8)
+            s2 = (127 - ge.integers(3, 6, size=(H, I // 32))).astype(np.uint8)
+            experts.append((_e4m3_bytes(w13i / 2), s13, _e4m3_bytes(w2i / 2), s2))
+        else:
+            raise ValueError(wdtype)
+    return dict(x_bits=to_bf16_bits(x), ids=ids, tw=tw, experts=experts)

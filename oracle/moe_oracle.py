@@ -20,8 +20,8 @@ optimisations for SageMaker AI on H200):
   align        expert histogram, padding of each expert's row count to a
                multiple of the block size, exclusive prefix sum and a stable
                scatter of flat slot ids into expert-sorted, block-padded order
-               (P2, section 1.1: ``sorted_token_ids``, ``num_tokens_post_padded``
-               and "GEMM fills padding inside active blocks").
+               (P2, section 1.1: ``sorted_token_ids``, ``num_tokens_post_padded``,
+               and the GEMM computing the padding rows of the blocks it runs).
   quant_act    dynamic fp8-e4m3 quantisation with one power-of-two scale per
                row and 128-column group (P2, section 1.2, the fused
                SiLU-mul-quant kernel: amax, floor 1e-10, times 1/448, rounded up
@@ -74,6 +74,7 @@ __all__ = [
     "round_bf16", "bf16_bits_to_f64", "round_e4m3", "e4m3_decode",
     "e4m3_encode", "fl32", "pow2_ceil", "fp8_group_scale", "quant_act",
     "route", "align", "align_capacity", "dequant_block", "forward", "expert_rows",
+    "expert_intermediate",
     "MX_BLOCK", "e8m0_decode", "e8m0_encode", "dequant_mx",
 ]
 
@@ -405,23 +406,41 @@ def forward(x, w13, w2, topk_ids, topk_weights, *, mode: str = "method",
     return out
 
 
+def expert_intermediate(x, w13_e, rows_tok, rows_tw, *, mode="method", fp8=False,
+                        group: int = 128, weight_on_input: bool = False, clamp_limit=None):
+    """The rows one expert hands its down GEMM, for the given tokens: the
+    gate/up GEMM, the SiLU-gated multiply with its rounding points and, with
+    ``fp8``, the per-row re-quantisation of P2 section 1.2 (options as for
+    ``forward``).  Returns a dict with
+      h       fp64 [rows, 2I]   gate/up results before any rounding;
+      a       fp64 [rows, I]    the SiLU-gated product (bf16 values in method mode);
+      codes   uint8 [rows, I]   e4m3 codes of ``a`` (fp8 and method mode only);
+      scales  fp64 [rows, I/group] their power-of-two group scales;
+      deq     fp64 [rows, I]    what the down GEMM multiplies (codes * scales,
+                                or ``a``)."""
+    method = mode == "method"
+    xt = np.asarray(x, dtype=np.float64)[rows_tok]
+    if fp8 and method:
+        xt = quant_act(xt, group)[2]
+    if weight_on_input:
+        xt = xt * np.asarray(rows_tw, dtype=np.float64)[:, None]
+    I = w13_e.shape[0] // 2
+    h = xt @ np.asarray(w13_e, dtype=np.float64).T
+    a = _silu_mul(h[:, :I], h[:, I:], method, clamp_limit)
+    out = dict(h=h, a=a, codes=None, scales=None, deq=a)
+    if fp8 and method:
+        out["codes"], out["scales"], out["deq"] = quant_act(a, group)
+    return out
+
+
 def expert_rows(x, w13_e, w2_e, rows_tok, rows_tw, *, mode="method", fp8=False,
                 group: int = 128, weight_on_input: bool = False, clamp_limit=None):
     """Contribution y = tw * W2[e] . act(W13[e] . x_t) of one expert to the
     given tokens (used to evaluate sampled outputs of large layers one expert
     at a time), with the options of ``forward``.  Returns [len(rows_tok), H]
     fp64."""
-    method = mode == "method"
-    xt = np.asarray(x, dtype=np.float64)[rows_tok]
-    if fp8 and method:
-        xt = quant_act(xt, group)[2]
-    w_rows = np.asarray(rows_tw, dtype=np.float64)[:, None]
-    if weight_on_input:
-        xt = xt * w_rows
-    I = w13_e.shape[0] // 2
-    h = xt @ np.asarray(w13_e, dtype=np.float64).T
-    a = _silu_mul(h[:, :I], h[:, I:], method, clamp_limit)
-    if fp8 and method:
-        a = quant_act(a, group)[2]
+    a = expert_intermediate(x, w13_e, rows_tok, rows_tw, mode=mode, fp8=fp8, group=group,
+                            weight_on_input=weight_on_input, clamp_limit=clamp_limit)["deq"]
     y = a @ np.asarray(w2_e, dtype=np.float64).T
+    w_rows = np.asarray(rows_tw, dtype=np.float64)[:, None]
     return y if weight_on_input else y * w_rows
