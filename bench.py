@@ -12,8 +12,11 @@ moe_forward alone.
 
 Prints one JSON line.  ``value`` is tokens/s of the whole step; ``roofline``
 describes the dominant kernel (GEMM1), timed with HIP events recorded on the
-stream it runs on; ``cpu_baseline`` is the fp64 oracle on a bounded token
-sample on this host.
+stream it runs on; ``layer`` the whole step against the layer's roofline;
+``cpu_baseline`` is the fp64 oracle on a bounded token sample on this host.
+The default run (the decode layer) also times the prefill layer (T=4096,
+E=128, H=4096, I=1536, top-8, bf16) and adds it as ``prefill``: the metric's
+second half, its matrix-core fraction (``--no-prefill`` skips it).
 """
 from __future__ import annotations
 
@@ -37,6 +40,8 @@ HBM_PEAK_GBS = 8000.0
 # weights' own type
 GEMM1_PEAK_TFLOPS = 2500.0
 GEMM2_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}
+# dense peak of the layer's own weight type (what an fp8 layer is graded on)
+LAYER_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -59,6 +64,9 @@ def parse():
     ap.add_argument("--decode-layer", action="store_true",
                     help="run each step as one moe_decode_layer launch (routing inside the kernel)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill record the default decode run adds")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region run one plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -99,14 +107,38 @@ def main():
               "single MI355X; multi-GPU sharding is described, not run.", file=sys.stderr)
         sys.exit(2)
 
+    rec = measure(args, args.workload, args.tokens, args.steps, args.warmup, not args.no_cpu_baseline,
+                  args.copy_calibration)
+    if args.workload == "decode" and not args.tokens and not args.no_prefill and not args.decode_layer:
+        # the metric's prefill half: the prefill layer's matrix-core fraction,
+        # timed in the same run (fewer steps: 2 ms each)
+        import gc
+        import torch
+        gc.collect()
+        torch.cuda.empty_cache()
+        p = measure(args, "prefill", None, args.prefill_steps, 2, False, False)
+        rec["prefill"] = {
+            "workload": p["config"]["workload"], "steps": p["steps"], "warmup": p["warmup"],
+            "ms_per_step": p["ms_per_step"], "tokens_per_s": p["value"],
+            "mfma_frac": p["layer"]["mfma_frac"], "hbm_frac": p["layer"]["hbm_frac"],
+            "tflops": p["layer"]["tflops"], "roofline_frac": p["layer"]["roofline_frac"],
+            "gemm1": {k: p["roofline"][k] for k in ("kernel", "kernel_ms", "mfma_frac", "hbm_frac", "traffic")},
+            "gemm2_ms": p["layer"]["stage_ms"]["gemm2"], "stage_ms": p["layer"]["stage_ms"],
+            "active_experts": p["layer"]["active_experts"],
+        }
+    print(json.dumps(rec), flush=True)
+
+
+def measure(args, workload, tokens, steps, warmup, with_cpu, copy_calibration):
+    """Time one workload; returns its JSON record (without printing it)."""
     import torch
     from moe_layer_amd import ops
     from moe_layer_amd.workloads import CONFIGS, Workload
 
     d = torch.device("cuda", 0)
-    cfg = CONFIGS[args.workload]
-    if args.tokens:
-        cfg = cfg.with_tokens(args.tokens)
+    cfg = CONFIGS[workload]
+    if tokens:
+        cfg = cfg.with_tokens(tokens)
     wl = Workload(cfg)
     fp8 = cfg.wdtype in ("fp8", "mxfp8")
     mx = cfg.wdtype == "mxfp8"
@@ -162,7 +194,7 @@ def main():
         else:
             w13[e].copy_(torch.from_numpy(c13.view(np.int16)).view(torch.bfloat16))
             w2[e].copy_(torch.from_numpy(c2.view(np.int16)).view(torch.bfloat16))
-        if e in cpu_experts and not args.no_cpu_baseline:
+        if e in cpu_experts and with_cpu:
             host_keep[e] = w
 
     wl.expert_weights_many(active.tolist(), put)
@@ -203,30 +235,30 @@ def main():
         if st != 0:
             raise RuntimeError(ops.status_string(st))
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
+    log(f"timing {steps} steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record()
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = ev0.elapsed_time(ev1) / steps
 
     # per-stage durations on the stream the kernels run on
     n_ev = ops.MOE_NUM_STAGES + 1
     stage_ms = np.zeros(ops.MOE_NUM_STAGES)
-    for _ in range(args.steps):
+    for _ in range(steps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         ops.moe_forward_profiled(fargs, ws, evs)
         torch.cuda.synchronize()
         stage_ms += np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(ops.MOE_NUM_STAGES)])
-    stage_ms /= args.steps
+    stage_ms /= steps
 
-    if args.copy_calibration:
+    if copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=d)
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -254,8 +286,11 @@ def main():
     g1_ms = stage_ms[2]
     # The dominant kernel's roofline: its lower bound is the larger of
     # (algorithmic bytes / HBM peak) and (flops / MFMA peak); report against
-    # that bound, and both fractions beside it.
-    peak_tf = GEMM1_PEAK_TFLOPS
+    # that bound, and both fractions beside it.  The peak is the dense peak of
+    # the layer's weight type (fp8 layers: 5.0 PF/s, although their GEMM1
+    # multiplies on the bf16 cores; that instruction's own ceiling is reported
+    # beside it as mfma_frac_instr).
+    peak_tf = LAYER_PEAK_TFLOPS[cfg.wdtype]
     g1_gbs = g1_bytes / (g1_ms * 1e-3) / 1e9
     g1_tfs = g1_flops / (g1_ms * 1e-3) / 1e12
     hbm_bound = g1_bytes / (HBM_PEAK_GBS * 1e9) >= g1_flops / (peak_tf * 1e12)
@@ -267,7 +302,7 @@ def main():
                 "frac": round(g1_tfs / peak_tf, 4)}
     large = plan["path"] == 2
     digest = kernel_source_digest("large" if large else "mx" if mx else "small")
-    roof["traffic"] = read_traffic(cfg.name if not args.tokens else f"{cfg.name}@{T}", digest)
+    roof["traffic"] = read_traffic(cfg.name if not tokens else f"{cfg.name}@{T}", digest)
     roof["kernel"] = ("gemm_large_kernel<1> (LDS-tiled GEMM1 + SiLU-mul epilogue)" if large
                       else "gemm1_mx_kernel (weight-streaming MXFP8 GEMM1 + SiLU-mul-quant epilogue)" if mx
                       else "gemm1_small_kernel (weight-streaming GEMM1 + SiLU-mul epilogue)")
@@ -276,6 +311,8 @@ def main():
     roof["algorithmic_flops"] = g1_flops
     roof["hbm_frac"] = round(g1_gbs / HBM_PEAK_GBS, 4)
     roof["mfma_frac"] = round(g1_tfs / peak_tf, 4)
+    roof["mfma_frac_instr"] = round(g1_tfs / GEMM1_PEAK_TFLOPS, 4)
+    roof["scope"] = "one kernel (GEMM1 + epilogue); the whole step's fractions are in 'layer'"
     if use_dl:
         # one launch per step: the dominant kernel is the whole layer
         if int(sync.abs().sum()) != 0:
@@ -286,19 +323,19 @@ def main():
                 "kernel": "decode_layer_kernel (route, align, GEMM1 + SiLU-mul, GEMM2, combine in one launch)",
                 "kernel_ms": round(float(ms), 5), "algorithmic_bytes": int(layer_bytes),
                 "algorithmic_flops": layer_flops, "hbm_frac": round(l_gbs / HBM_PEAK_GBS, 4),
-                "mfma_frac": None}
+                "mfma_frac": None, "scope": "the whole layer (one launch)"}
 
     mfma_floor_s = g1_flops / (GEMM1_PEAK_TFLOPS * 1e12) + (layer_flops - g1_flops) / (
         GEMM2_PEAK_TFLOPS[cfg.wdtype] * 1e12)
 
     # ---- CPU baseline: the oracle on a bounded sample ---------------------
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         cpu = cpu_baseline(cfg, wl, ids_host, tw.cpu().numpy(), host_keep, n_cpu, logits is not None)
 
     rec = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.wdtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name} MoE layer T={T} E={E} H={H} I={I} topk={k} {cfg.wdtype}",
                    "T": T, "E": E, "H": H, "I": I, "topk": k, "weights": cfg.wdtype,
@@ -313,13 +350,16 @@ def main():
                   "hbm_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
-                  # matrix-core floor: GEMM1's flops at the bf16 peak plus GEMM2's at its type's
-                  "mfma_frac": round(mfma_floor_s / (ms * 1e-3), 4),
-                  "roofline_frac": round(max(layer_bytes / (HBM_PEAK_GBS * 1e9), mfma_floor_s) / (ms * 1e-3), 4),
+                  # against the dense peak of the weight type (fp8: 5.0 PF/s)
+                  "mfma_frac": round(layer_flops / (LAYER_PEAK_TFLOPS[cfg.wdtype] * 1e12) / (ms * 1e-3), 4),
+                  # against the instructions the kernels use (GEMM1 on bf16 cores, GEMM2 on the weight type's)
+                  "mfma_frac_instr": round(mfma_floor_s / (ms * 1e-3), 4),
+                  "roofline_frac": round(max(layer_bytes / (HBM_PEAK_GBS * 1e9),
+                                             layer_flops / (LAYER_PEAK_TFLOPS[cfg.wdtype] * 1e12)) / (ms * 1e-3), 4),
                   "stage_ms": {n: round(float(v), 5) for n, v in zip(ops.STAGE_NAMES, stage_ms)},
                   "kernel_digest": digest},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def cpu_baseline(cfg, wl, ids, tw32, host_w, n, routed_from_logits):

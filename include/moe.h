@@ -111,8 +111,8 @@ MOE_API int64_t moe_align_capacity(int32_t T, int32_t topk, int32_t E, int32_t b
 /*
  * moe_align — token-to-expert alignment into expert-sorted, block-padded
  * order (P2 section 1.1: sorted_token_ids, num_tokens_post_padded, and the
- * per-block expert of the block-sorted GEMM, where "GEMM fills padding
- * inside active blocks").
+ * per-block expert of the block-sorted GEMM, which computes the padding rows
+ * of the blocks it runs).
  *
  * With flat slot ids f = t*topk + j, c_e = #{f : topk_ids[f] == e} and
  * P_e = ceil(c_e / block_m) * block_m, o_e = sum_{e' < e} P_e':
@@ -137,6 +137,35 @@ MOE_API int64_t moe_align_capacity(int32_t T, int32_t topk, int32_t E, int32_t b
 MOE_API int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E,
                       int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
                       int32_t* num_tokens_post_padded, int32_t* inv, hipStream_t stream);
+
+/*
+ * moe_align_scratch_bytes — device scratch bytes moe_align_ws needs for
+ * T * topk routed slots over E experts: 0 below 2048 slots (one workgroup
+ * aligns them, as moe_align does), else the per-workgroup expert counts and
+ * starts of the multi-workgroup form (2 * ceil(T*topk / 1024) * E int32,
+ * rounded up to 256 bytes).  Host only; negative status on invalid arguments.
+ */
+MOE_API int64_t moe_align_scratch_bytes(int32_t T, int32_t topk, int32_t E);
+
+/*
+ * moe_align_ws — moe_align (same definition, same outputs bit for bit) on
+ * many workgroups: from 2048 routed slots on, one workgroup per 1024 slots
+ * counts its slots per expert, one workgroup scans the counts into padded
+ * expert offsets and per-workgroup starts, and the counting workgroups
+ * scatter their slots (stable: ascending flat index within an expert).
+ * Below 2048 slots it is moe_align.  One workgroup's ALUs bound moe_align
+ * above a few thousand slots (the prefill layer's 32768 slots: 63 against
+ * 27 us for the multi-workgroup form).
+ *
+ *   scratch        device, >= moe_align_scratch_bytes(T, topk, E) bytes,
+ *                  4-byte aligned (may be NULL when that is 0); contents on
+ *                  entry do not matter; owned by the caller
+ *   other arguments as for moe_align.
+ * MOE_ERR_WORKSPACE when the scratch is missing, misaligned or too small.
+ */
+MOE_API int moe_align_ws(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E, int32_t block_m,
+                         int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                         int32_t* inv, void* scratch, int64_t scratch_bytes, hipStream_t stream);
 
 /*
  * moe_quant_act — dynamic fp8 quantisation of bf16 activations, one
@@ -223,7 +252,11 @@ typedef struct moe_forward_args {
                              (+inf allowed, the same as none) */
 } moe_forward_args;
 
-/* What moe_forward will do for a set of arguments (the test spy). */
+/* What moe_forward will do for a set of arguments: the tile path, block size
+ * and launch shapes it picks, so that a test can check which path a shape
+ * takes without timing it (the role of the spy that P2 section 1.1's test
+ * patches onto the A_is_sorted decision to see whether the sorted-A path
+ * ran), plus the workspace offsets of the intermediates. */
 typedef struct moe_plan_info {
     int32_t path;          /* MOE_PATH_SMALL_M or MOE_PATH_LARGE_M */
     int32_t block_m;       /* rows per expert block */
@@ -238,8 +271,11 @@ typedef struct moe_plan_info {
     int64_t off_xq, off_xs, off_inter, off_inter_scale, off_y;
 } moe_plan_info;
 
-/* moe_plan — fill *out for these arguments (host only, no device work).
- * Pointers in *a are not inspected.  Returns a status. */
+/* moe_plan — fill *out for these arguments (host only, no device work):
+ * the decisions moe_forward takes for them, reported instead of observed
+ * (P2 section 1.1's test spies on the sorted-A decision; here the planner's
+ * choice is a pure function a test can call).  Pointers in *a are not
+ * inspected.  Returns a status. */
 MOE_API int moe_plan(const moe_forward_args* a, moe_plan_info* out);
 
 /* moe_forward_workspace — workspace bytes moe_forward needs for these

@@ -399,9 +399,11 @@ __device__ __forceinline__ void gemm2_mx_tiles(const GemmArgs& g, int blk, int t
     set_scale_lane(ad, g, lr, lk, kbi);
     ad.b = static_cast<const uint8_t*>(g.inter) + int64_t(blk) * BM * I;
 
-    // the block's token-scale table, all of K at once
+    // the block's token-scale table, all of K at once (the barrier first: a
+    // workgroup that ran an item before must have finished reading it)
     __shared__ __attribute__((aligned(16))) uint8_t tab[BM * kTabStride];
     {
+        __syncthreads();
         const uint8_t* scales = reinterpret_cast<const uint8_t*>(g.inter_scale) + int64_t(blk) * BM * kbi;
         for (int i = threadIdx.x; i < BM * ns; i += NW * 64) {
             const int r = i / ns, k = i - r * ns;

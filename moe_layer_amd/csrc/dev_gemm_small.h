@@ -487,9 +487,11 @@ __device__ __forceinline__ void gemm2_tiles(const GemmArgs& g, int blk, int tile
                      : nullptr;
     }
 
-    // fp8: the block's token-scale table, all of K at once
+    // fp8: the block's token-scale table, all of K at once (the barrier first:
+    // a workgroup that ran an item before must have finished reading it)
     __shared__ float tab[FP8 ? BM * kTabStride : 1];
     if constexpr (FP8) {
+        __syncthreads();
         const float* scales = g.inter_scale + int64_t(blk) * BM * kb_count;
         for (int i = threadIdx.x; i < BM * ns; i += NW * 64) {
             const int r = i / ns, k = i - r * ns;

@@ -14,8 +14,9 @@ using namespace moe;
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 4;   // 1.1: MXFP8 weights; 1.2: layer variants; 1.3: moe_decode_layer;
-                                   // 1.4: packed MXFP8 scales (moe_pack_mx_scales)
+constexpr int kVersionMinor = 5;   // 1.1: MXFP8 weights; 1.2: layer variants; 1.3: moe_decode_layer;
+                                   // 1.4: packed MXFP8 scales (moe_pack_mx_scales);
+                                   // 1.5: multi-workgroup alignment (moe_align_ws)
 // Rows per expert (on average) from which the LDS-tiled path beats weight
 // streaming.  Measured with bf16 weights (align + GEMM1 + GEMM2): E 128, H
 // 4096, I 1536 at 8 rows 0.90 ms streaming vs 1.08 tiled, 16 rows 1.14 vs 1.09,
@@ -209,6 +210,32 @@ MOE_API int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t 
     if (T > 0 && (!topk_ids || !aligned(topk_ids, 4))) return MOE_ERR_INVALID_ARG;
     return hip_status(launch_align(topk_ids, T, topk, E, block_m, cap, sorted_token_ids, expert_ids,
                                    num_tokens_post_padded, inv, stream));
+}
+
+MOE_API int64_t moe_align_scratch_bytes(int32_t T, int32_t topk, int32_t E) {
+    if (T < 0 || topk < 1 || topk > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+    const int64_t R = int64_t(T) * topk;
+    if (R > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    return R >= kAlignWideMinSlots ? round_up(align_scratch_bytes(R, E), 256) : 0;
+}
+
+MOE_API int moe_align_ws(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E, int32_t block_m,
+                         int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                         int32_t* inv, void* scratch, int64_t scratch_bytes, hipStream_t stream) {
+    const int64_t cap = moe_align_capacity(T, topk, E, block_m);
+    if (cap < 0) return int(cap);
+    const int64_t need = moe_align_scratch_bytes(T, topk, E);
+    if (need < 0) return int(need);
+    if (need == 0)
+        return moe_align(topk_ids, T, topk, E, block_m, sorted_token_ids, expert_ids, num_tokens_post_padded, inv,
+                         stream);
+    if (!sorted_token_ids || !expert_ids || !num_tokens_post_padded || !aligned(sorted_token_ids, 4) ||
+        !aligned(expert_ids, 4) || !aligned(num_tokens_post_padded, 4) || (inv && !aligned(inv, 4)) ||
+        !topk_ids || !aligned(topk_ids, 4))
+        return MOE_ERR_INVALID_ARG;
+    if (!scratch || !aligned(scratch, 4) || scratch_bytes < need) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_align_wide(topk_ids, T, topk, E, block_m, cap, sorted_token_ids, expert_ids,
+                                        num_tokens_post_padded, inv, scratch, stream));
 }
 
 MOE_API int moe_quant_act(const void* x, int32_t rows, int32_t cols, uint8_t* codes, float* scales,

@@ -24,6 +24,7 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_QUANT_GROUP, MOE_MX_BLOCK = 1024, 64, 128, 32
 
 # every entry point include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_version", "moe_route", "moe_align_capacity", "moe_align",
+           "moe_align_scratch_bytes", "moe_align_ws",
            "moe_quant_act", "moe_quant_act_mx", "moe_pack_mx_scales", "moe_plan", "moe_forward_workspace", "moe_forward",
            "moe_forward_profiled", "moe_decode_layer")
 MOE_NUM_STAGES = 5
@@ -73,6 +74,10 @@ def lib() -> C.CDLL:
         L.moe_align_capacity.argtypes = [i32, i32, i32, i32]
         L.moe_align.restype = C.c_int
         L.moe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.moe_align_scratch_bytes.restype = i64
+        L.moe_align_scratch_bytes.argtypes = [i32, i32, i32]
+        L.moe_align_ws.restype = C.c_int
+        L.moe_align_ws.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp]
         L.moe_quant_act.restype = C.c_int
         L.moe_quant_act.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_quant_act_mx.restype = C.c_int
@@ -149,6 +154,32 @@ def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, with_inv: bool = Tru
     inv = torch.empty(T * k, dtype=torch.int32, device=dev) if with_inv else None
     _check("moe_align", lib().moe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids), _ptr(expert_ids),
                                         _ptr(ntpp), _ptr(inv), _stream(dev)))
+    return dict(sorted_token_ids=sorted_ids, expert_ids=expert_ids, num_tokens_post_padded=ntpp, inv=inv)
+
+
+def moe_align_scratch_bytes(T: int, topk: int, E: int) -> int:
+    n = lib().moe_align_scratch_bytes(T, topk, E)
+    if n < 0:
+        raise MoeError("moe_align_scratch_bytes", int(n))
+    return int(n)
+
+
+def moe_align_ws(topk_ids: torch.Tensor, E: int, block_m: int, with_inv: bool = True, scratch=None):
+    """moe_align on many workgroups (from 2048 routed slots; the same outputs)."""
+    assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous() and topk_ids.dim() == 2
+    T, k = topk_ids.shape
+    cap = moe_align_capacity(T, k, E, block_m)
+    dev = topk_ids.device
+    need = moe_align_scratch_bytes(T, k, E)
+    if scratch is None and need > 0:
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev)
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(-(-cap // block_m), dtype=torch.int32, device=dev)
+    ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev) if with_inv else None
+    _check("moe_align_ws", lib().moe_align_ws(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids), _ptr(expert_ids),
+                                              _ptr(ntpp), _ptr(inv), _ptr(scratch),
+                                              0 if scratch is None else scratch.numel(), _stream(dev)))
     return dict(sorted_token_ids=sorted_ids, expert_ids=expert_ids, num_tokens_post_padded=ntpp, inv=inv)
 
 
@@ -272,23 +303,52 @@ def moe_forward_profiled(args: ForwardArgs, workspace: torch.Tensor, events, str
 _SYNC = {}
 
 
-def decode_sync(device) -> torch.Tensor:
-    """A zeroed barrier buffer for moe_decode_layer on ``device`` (kept per
-    device and reused: every call leaves it zero)."""
-    key = torch.device(device).index or 0
+def decode_sync(device, stream=None) -> torch.Tensor:
+    """A zeroed barrier buffer for moe_decode_layer, kept per (device, stream)
+    and reused: every call leaves it zero, and calls that share a buffer must
+    be ordered on one stream (include/moe.h)."""
+    dev = torch.device(device)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    key = (dev.index or 0, int(s.cuda_stream))
     if key not in _SYNC:
-        _SYNC[key] = torch.zeros(MOE_SYNC_WORDS, dtype=torch.int32, device=device)
+        _SYNC[key] = torch.zeros(MOE_SYNC_WORDS, dtype=torch.int32, device=dev)
     return _SYNC[key]
+
+
+class DecodeLayerTimeout(MoeError):
+    """A grid-barrier wait of moe_decode_layer exceeded its bound (the device
+    could not keep every workgroup resident): that call's output is undefined."""
+
+    def __init__(self, word: int):
+        self.word = word
+        RuntimeError.__init__(self, f"moe_decode_layer: a grid-barrier wait timed out (sync[MOE_SYNC_ERROR] = "
+                                    f"{word}); the output of that call is undefined")
+        self.status = MOE_ERR_HIP
+
+
+def decode_layer_status(sync: torch.Tensor) -> None:
+    """Check a moe_decode_layer barrier buffer after the calls that used it:
+    reads sync[MOE_SYNC_ERROR] (this waits for the buffer's stream), and if a
+    barrier wait timed out re-zeroes the buffer, as include/moe.h requires
+    before its next use, and raises DecodeLayerTimeout.  While that word is
+    set, the outputs of the calls since it was last clear are invalid."""
+    word = int(sync[MOE_SYNC_ERROR].item())
+    if word != 0:
+        sync.zero_()
+        raise DecodeLayerTimeout(word)
 
 
 def moe_decode_layer(x, w13, w2, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
                      router_logits=None, topk=None, renormalize=True, out=None, workspace=None, sync=None,
-                     weight_on_input=False, clamp_limit=0.0, mx_packed_scales=False):
+                     weight_on_input=False, clamp_limit=0.0, mx_packed_scales=False, check=True):
     """The layer for few tokens as one kernel launch (the weight-streaming
     path with 16-row blocks).  With fp32 ``router_logits`` [T,E] it routes
     them (top ``topk``) into topk_ids / topk_weights (allocated when None);
-    else it uses the given routing.  Returns (out, topk_ids, topk_weights,
-    workspace)."""
+    else it uses the given routing.  ``sync``: the barrier buffer (default:
+    one per device and current stream).  With ``check`` the call waits for
+    the stream and raises DecodeLayerTimeout if a barrier wait timed out
+    (decode_layer_status); without it, call decode_layer_status before
+    trusting the output.  Returns (out, topk_ids, topk_weights, workspace)."""
     T, H = x.shape
     dev = x.device
     if out is None:
@@ -309,4 +369,6 @@ def moe_decode_layer(x, w13, w2, topk_ids=None, topk_weights=None, w13_scale=Non
         st = lib().moe_decode_layer(C.byref(a), None, 0, None, None, _ptr(sync), _ptr(workspace),
                                     workspace.numel(), _stream(dev))
     _check("moe_decode_layer", st)
+    if check:
+        decode_layer_status(sync)
     return out, topk_ids, topk_weights, workspace

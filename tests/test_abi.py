@@ -260,3 +260,48 @@ def test_decode_layer_validation():
     assert call(_args(), nbytes=16) == ops.MOE_ERR_WORKSPACE
     assert call(_args(T=0, ptr=None), sync=None, ws=None) in (ops.MOE_OK, ops.MOE_ERR_INVALID_ARG)
     del f
+
+
+@pytest.mark.parametrize("T,k,E", [(0, 8, 16), (255, 8, 64), (256, 8, 64), (4096, 8, 128), (8192, 8, 256),
+                                   (1000, 64, 1024)])
+def test_align_scratch_bytes(T, k, E):
+    R = T * k
+    n = ops.moe_align_scratch_bytes(T, k, E)
+    if R < 2048:
+        assert n == 0
+    else:
+        groups = -(-R // 1024)
+        assert n >= 2 * groups * E * 4 and n % 256 == 0
+
+
+def test_align_ws_validation():
+    L = ops.lib()
+    assert L.moe_align_scratch_bytes(-1, 8, 16) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align_scratch_bytes(16, 0, 16) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align_scratch_bytes(16, 8, 1025) == ops.MOE_ERR_INVALID_ARG
+    need = L.moe_align_scratch_bytes(4096, 8, 128)
+    ptrs = [C.c_void_p(FAKE)] * 4
+    # scratch missing, too small, misaligned: rejected before any device work
+    assert L.moe_align_ws(C.c_void_p(FAKE), 4096, 8, 128, 64, *ptrs, None, 0, None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_align_ws(C.c_void_p(FAKE), 4096, 8, 128, 64, *ptrs, C.c_void_p(FAKE), need - 4,
+                          None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_align_ws(C.c_void_p(FAKE), 4096, 8, 128, 64, *ptrs, C.c_void_p(FAKE + 2), need,
+                          None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_align_ws(None, 4096, 8, 128, 64, *ptrs, C.c_void_p(FAKE), need, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_align_ws(C.c_void_p(FAKE), 4096, 8, 128, 0, *ptrs, C.c_void_p(FAKE), need,
+                          None) == ops.MOE_ERR_INVALID_ARG
+
+
+def test_decode_layer_status_word():
+    """decode_layer_status raises when the barrier buffer's error word is set
+    (as the kernel leaves it after a timed-out wait) and re-zeroes the buffer;
+    a clean buffer passes.  The word is set from the host here."""
+    import torch
+    sync = torch.zeros(ops.MOE_SYNC_WORDS, dtype=torch.int32)
+    ops.decode_layer_status(sync)
+    sync[ops.MOE_SYNC_ERROR] = 1
+    sync[3] = 7
+    with pytest.raises(ops.DecodeLayerTimeout) as ei:
+        ops.decode_layer_status(sync)
+    assert ei.value.status == ops.MOE_ERR_HIP and "undefined" in str(ei.value)
+    assert int(sync.abs().sum()) == 0

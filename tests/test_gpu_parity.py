@@ -82,6 +82,26 @@ def test_align_workloads(name, B):
     _check_align(ids, cfg.E, B)
 
 
+@pytest.mark.parametrize("T,k,E,B", [(100, 8, 64, 16), (256, 8, 64, 16), (4096, 8, 128, 64), (4096, 8, 128, 256),
+                                     (8192, 8, 256, 16), (3000, 3, 5, 16), (2000, 64, 40, 7), (999, 5, 1024, 16)])
+def test_align_ws_multi_workgroup(T, k, E, B):
+    """moe_align_ws (many workgroups from 2048 slots on, one below) gives the
+    oracle's alignment bit for bit, inverse permutation included, also on a
+    scratch buffer poisoned with 0xFF bytes."""
+    rng = np.random.default_rng(T * 7 + E + B)
+    ids = rng.integers(-2, E + 2, size=(T, k))
+    ids[: T // 4, 0] = rng.integers(0, max(1, E // 16), size=T // 4)   # skewed load
+    ids_t = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev())
+    need = ops.moe_align_scratch_bytes(T, k, E)
+    scratch = torch.full((max(need, 256),), 0xFF, dtype=torch.uint8, device=dev())
+    a = ops.moe_align_ws(ids_t, E, B, scratch=scratch)
+    o = O.align(ids, E, B)
+    np.testing.assert_array_equal(a["sorted_token_ids"].cpu().numpy(), o["sorted_token_ids"])
+    np.testing.assert_array_equal(a["expert_ids"].cpu().numpy(), o["expert_ids"])
+    assert int(a["num_tokens_post_padded"].item()) == o["num_tokens_post_padded"]
+    np.testing.assert_array_equal(a["inv"].cpu().numpy(), o["inv"])
+
+
 def test_align_empty_experts_worked_example():
     _check_align(np.array([[3, 1], [1, 3]]), 4, 2)
 
