@@ -98,13 +98,16 @@ def _binade(v: np.ndarray) -> np.ndarray:
 def _round_to_grid(v: np.ndarray, min_normal_exp: int, mant_bits: int) -> np.ndarray:
     """Round fp64 values to the nearest value with ``mant_bits`` fraction bits
     (normal range) or the subnormal quantum below ``min_normal_exp``; ties to
-    even.  Division and multiplication by the power-of-two quantum are exact."""
+    even.  Division and multiplication by the power-of-two quantum are exact.
+    A zero keeps its sign, and so does a value that rounds to zero, as in an
+    IEEE conversion (a cast of -0.0 gives the negative-zero code)."""
     v = np.asarray(v, dtype=np.float64)
     out = np.zeros_like(v)
+    np.copysign(out, v, out=out)
     nz = (v != 0) & np.isfinite(v)
     e = np.maximum(_binade(v[nz]), min_normal_exp)
     q = np.ldexp(1.0, (e - mant_bits).astype(np.int64))
-    out[nz] = np.rint(v[nz] / q) * q           # np.rint rounds half to even
+    out[nz] = np.copysign(np.rint(v[nz] / q) * q, v[nz])   # np.rint rounds half to even
     out[~np.isfinite(v)] = v[~np.isfinite(v)]
     return out
 

@@ -109,8 +109,23 @@ def test_e4m3_matches_torch_cast():
     ref = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
     np.testing.assert_array_equal(O.round_e4m3(v.astype(np.float64)), ref)
     ref_codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    nz = ref != 0                             # torch and we agree on signed zeros too
-    np.testing.assert_array_equal(O.e4m3_encode(O.round_e4m3(v.astype(np.float64)))[nz], ref_codes[nz])
+    # every code, values that round to a signed zero included
+    np.testing.assert_array_equal(O.e4m3_encode(O.round_e4m3(v.astype(np.float64))), ref_codes)
+
+
+def test_signed_zeros_keep_their_sign():
+    """A cast keeps the sign of zero, also for values that round to zero:
+    -0.0 and -2^-11 give the negative-zero codes (e4m3 0x80, bf16 0x8000), as
+    torch's casts do."""
+    v = np.array([0.0, -0.0, 2.0 ** -11, -(2.0 ** -11), -(2.0 ** -10)], np.float32)
+    ref_e4m3 = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_encode(O.round_e4m3(v.astype(np.float64))), ref_e4m3)
+    assert list(ref_e4m3[:4]) == [0x00, 0x80, 0x00, 0x80]
+    tiny = np.array([0.0, -0.0, -(2.0 ** -140)], np.float32)
+    ref_bf16 = torch.from_numpy(tiny).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = O.round_bf16(tiny.astype(np.float64))
+    np.testing.assert_array_equal(np.signbit(ours), (ref_bf16 & 0x8000) != 0)
+    np.testing.assert_array_equal(ours, O.bf16_bits_to_f64(ref_bf16))
 
 
 def test_fl32_is_correctly_rounded_multiply():
