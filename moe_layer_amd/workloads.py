@@ -268,13 +268,15 @@ def _e4m3_bytes(v: np.ndarray) -> np.ndarray:
 def exact_sum_layer(T: int, E: int, H: int, I: int, topk: int, wdtype: str, seed: int = 0,
                     pow2_route_weights: bool = False, hot_expert: int | None = None):
     """A seeded layer whose activations are i/8 with i uniform in [-7, 7] and
-    whose weights are j/32 with j uniform in [-3, 3] (bf16), or e4m3 codes of
-    j/2 times a power-of-two block scale drawn from {2^-3, 2^-4, 2^-5} (fp8:
-    per 128x128 block; MXFP8: an E8M0 byte per row and 32 K elements).  Every
-    product is a small integer times 2^-11 or coarser and |sum| < 2^24 of those
-    units for H < 2^16, so fp32 accumulation is exact in any order; x also
-    survives the fp8 activation quantisation unchanged (at most 3 significant
-    bits, scaled by a power of two).
+    whose weights are j/128 with j uniform in [-15, 15] (bf16), or e4m3 codes
+    of j/2 (4 significant bits at most) times a power-of-two block scale drawn
+    from {2^-5, 2^-6, 2^-7} (fp8: per 128x128 block; MXFP8: an E8M0 byte per
+    row and 32 K elements).  Every product is an integer of at most 105 times
+    2^-11 or coarser, and |sum| < 2^24 of those units for H < 2^17, so fp32
+    accumulation is exact in any order; the sums carry about 10 significant
+    bits, so bf16(h) is a real rounding.  x survives the fp8 activation
+    quantisation unchanged (at most 3 significant bits, scaled by a power of
+    two).
 
     Routing: ids uniform over [0, E) with duplicates, plus one unrouted slot
     (id -1) and one id E when T * topk > 4; ``hot_expert`` takes a third of
@@ -301,17 +303,17 @@ def exact_sum_layer(T: int, E: int, H: int, I: int, topk: int, wdtype: str, seed
     experts = []
     for e in range(E):
         ge = np.random.default_rng([seed, 100 + TID_W13, e])
-        w13i = ge.integers(-3, 4, size=(2 * I, H)).astype(np.float32)
-        w2i = ge.integers(-3, 4, size=(H, I)).astype(np.float32)
+        w13i = ge.integers(-15, 16, size=(2 * I, H)).astype(np.float32)
+        w2i = ge.integers(-15, 16, size=(H, I)).astype(np.float32)
         if wdtype == "bf16":
-            experts.append((to_bf16_bits(w13i / 32), None, to_bf16_bits(w2i / 32), None))
+            experts.append((to_bf16_bits(w13i / 128), None, to_bf16_bits(w2i / 128), None))
         elif wdtype == "fp8":
-            s13 = np.ldexp(1.0, -ge.integers(3, 6, size=(2 * I // 128, H // 128))).astype(np.float32)
-            s2 = np.ldexp(1.0, -ge.integers(3, 6, size=(H // 128, I // 128))).astype(np.float32)
+            s13 = np.ldexp(1.0, -ge.integers(5, 8, size=(2 * I // 128, H // 128))).astype(np.float32)
+            s2 = np.ldexp(1.0, -ge.integers(5, 8, size=(H // 128, I // 128))).astype(np.float32)
             experts.append((_e4m3_bytes(w13i / 2), s13, _e4m3_bytes(w2i / 2), s2))
         elif wdtype == "mxfp8":
-            s13 = (127 - ge.integers(3, 6, size=(2 * I, H // 32))).astype(np.uint8)
-            s2 = (127 - ge.integers(3, 6, size=(H, I // 32))).astype(np.uint8)
+            s13 = (127 - ge.integers(5, 8, size=(2 * I, H // 32))).astype(np.uint8)
+            s2 = (127 - ge.integers(5, 8, size=(H, I // 32))).astype(np.uint8)
             experts.append((_e4m3_bytes(w13i / 2), s13, _e4m3_bytes(w2i / 2), s2))
         else:
             raise ValueError(wdtype)
