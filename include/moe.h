@@ -343,6 +343,27 @@ MOE_API int moe_forward_profiled(const moe_forward_args* a, void* workspace, int
                                  hipStream_t stream, hipEvent_t* events, int32_t n_events);
 
 /*
+ * moe_forward_noalloc — moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Its workspace is a static device array inside the
+ * library, MOE_NOALLOC_MAX_BYTES long, of which every GPU the library runs
+ * on holds one copy until the process ends; the call itself allocates
+ * nothing.  The caller still passes the inputs and the output in *a.
+ *
+ * Same results as moe_forward (the same kernels, bit for bit) and the same
+ * argument errors, plus MOE_ERR_WORKSPACE when moe_forward_workspace(a)
+ * exceeds MOE_NOALLOC_MAX_BYTES (64 MiB: decode-sized layers, e.g. 16 tokens
+ * of 128 experts with H 4096 and I 1536 need 8.4 MB), and MOE_ERR_HIP if the
+ * array's device address cannot be found (looked up once per device, on the
+ * first call there).  Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  The array's contents on entry do not matter; it
+ * keeps the last call's intermediates.
+ */
+#define MOE_NOALLOC_MAX_BYTES (64 << 20)
+MOE_API int moe_forward_noalloc(const moe_forward_args* a, hipStream_t stream);
+
+/*
  * moe_decode_layer — the whole layer for few tokens (decode) in ONE kernel
  * launch: [router top-k from logits] and [fp8 activation quantisation] ->
  * alignment -> GEMM1 + SiLU-mul epilogue -> GEMM2 -> top-k combine, the phases

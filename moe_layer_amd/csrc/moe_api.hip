@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstddef>
+#include <mutex>
 
 #include "common.h"
 
@@ -14,9 +15,10 @@ using namespace moe;
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 5;   // 1.1: MXFP8 weights; 1.2: layer variants; 1.3: moe_decode_layer;
+constexpr int kVersionMinor = 6;   // 1.1: MXFP8 weights; 1.2: layer variants; 1.3: moe_decode_layer;
                                    // 1.4: packed MXFP8 scales (moe_pack_mx_scales);
-                                   // 1.5: multi-workgroup alignment (moe_align_ws)
+                                   // 1.5: multi-workgroup alignment (moe_align_ws);
+                                   // 1.6: moe_forward_noalloc
 // Rows per expert (on average) from which the LDS-tiled path beats weight
 // streaming.  Measured with bf16 weights (align + GEMM1 + GEMM2): E 128, H
 // 4096, I 1536 at 8 rows 0.90 ms streaming vs 1.08 tiled, 16 rows 1.14 vs 1.09,
@@ -410,3 +412,53 @@ MOE_API int moe_decode_layer(const moe_forward_args* a, const float* router_logi
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// moe_forward_noalloc: moe_forward with its workspace in a static device
+// array of MOE_NOALLOC_MAX_BYTES that the library holds on every GPU it runs
+// on, for callers that cannot allocate device memory.  Host code never passes
+// the array's name to a kernel or a copy: in host code that name is a host
+// stand-in, not the device address.  The device address is looked up once per
+// device with hipGetSymbolAddress and used from then on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's copy of the scratch array (nullptr on failure).
+void* scratch_for_current_device(int* status) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *status = MOE_ERR_HIP;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+        *status = MOE_ERR_HIP;
+        return nullptr;
+    }
+    *status = MOE_OK;
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" MOE_API int moe_forward_noalloc(const moe_forward_args* a, hipStream_t stream) {
+    Plan p;
+    int st = make_plan(a, &p);
+    if (st != MOE_OK) return st;
+    if (p.total > MOE_NOALLOC_MAX_BYTES) return MOE_ERR_WORKSPACE;   // beyond the static array
+    if (a->T == 0) return MOE_OK;
+    void* ws = scratch_for_current_device(&st);
+    if (!ws) return st;
+    return run_forward(a, ws, MOE_NOALLOC_MAX_BYTES, stream, nullptr);
+}

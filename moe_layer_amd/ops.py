@@ -26,8 +26,9 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_QUANT_GROUP, MOE_MX_BLOCK = 1024, 64, 128, 32
 EXPORTS = ("moe_status_string", "moe_version", "moe_route", "moe_align_capacity", "moe_align",
            "moe_align_scratch_bytes", "moe_align_ws",
            "moe_quant_act", "moe_quant_act_mx", "moe_pack_mx_scales", "moe_plan", "moe_forward_workspace", "moe_forward",
-           "moe_forward_profiled", "moe_decode_layer")
+           "moe_forward_profiled", "moe_decode_layer", "moe_forward_noalloc")
 MOE_NUM_STAGES = 5
+MOE_NOALLOC_MAX_BYTES = 64 << 20
 MOE_SYNC_WORDS, MOE_SYNC_ERROR = 640, 576
 STAGE_NAMES = ("align", "quant_act", "gemm1", "gemm2", "combine")
 
@@ -92,6 +93,8 @@ def lib() -> C.CDLL:
         L.moe_forward.argtypes = [C.POINTER(ForwardArgs), vp, i64, vp]
         L.moe_forward_profiled.restype = C.c_int
         L.moe_forward_profiled.argtypes = [C.POINTER(ForwardArgs), vp, i64, vp, C.POINTER(C.c_void_p), i32]
+        L.moe_forward_noalloc.restype = C.c_int
+        L.moe_forward_noalloc.argtypes = [C.POINTER(ForwardArgs), vp]
         L.moe_decode_layer.restype = C.c_int
         L.moe_decode_layer.argtypes = [C.POINTER(ForwardArgs), vp, i32, vp, vp, vp, vp, i64, vp]
         _lib = L
@@ -284,6 +287,21 @@ def moe_forward(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=Non
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _check("moe_forward", lib().moe_forward(C.byref(a), _ptr(workspace), workspace.numel(), _stream(x.device)))
     return out, workspace
+
+
+def moe_forward_noalloc(x, w13, w2, topk_ids, topk_weights, w13_scale=None, w2_scale=None, out=None,
+                        path=MOE_PATH_AUTO, block_m=0, weight_on_input=False, clamp_limit=0.0,
+                        mx_packed_scales=False):
+    """moe_forward with the library's static per-GPU workspace
+    (moe_forward_noalloc: for callers that cannot allocate device memory;
+    up to MOE_NOALLOC_MAX_BYTES of workspace).  Returns out."""
+    T, H = x.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    a = forward_args(x, w13, w2, topk_ids, topk_weights, w13_scale, w2_scale, out, path, block_m,
+                     weight_on_input=weight_on_input, clamp_limit=clamp_limit, mx_packed_scales=mx_packed_scales)
+    _check("moe_forward_noalloc", lib().moe_forward_noalloc(C.byref(a), _stream(x.device)))
+    return out
 
 
 def moe_forward_profiled(args: ForwardArgs, workspace: torch.Tensor, events, stream=None):

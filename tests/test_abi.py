@@ -305,3 +305,16 @@ def test_decode_layer_status_word():
         ops.decode_layer_status(sync)
     assert ei.value.status == ops.MOE_ERR_HIP and "undefined" in str(ei.value)
     assert int(sync.abs().sum()) == 0
+
+
+def test_forward_noalloc_rejects_layers_beyond_its_array():
+    """moe_forward_noalloc checks the workspace size against its static array
+    before any device work: a prefill-sized layer (0.66 GB of workspace) gets
+    MOE_ERR_WORKSPACE, invalid arguments their usual status."""
+    L = ops.lib()
+    a = _args(T=4096)
+    assert ops.moe_forward_workspace(a) > ops.MOE_NOALLOC_MAX_BYTES
+    assert L.moe_forward_noalloc(C.byref(a), None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_forward_noalloc(None, None) == ops.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(C.byref(_args(k=0)), None) == ops.MOE_ERR_INVALID_ARG
+    assert ops.moe_forward_workspace(_args()) <= ops.MOE_NOALLOC_MAX_BYTES     # the decode layer fits
