@@ -141,10 +141,16 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, const Ring& ring, in
 
     // the K walk starts at a stage that depends on (expert, tile), so that the
     // workgroups do not all read the same offset of their 2^k-byte rows at once
-    // (prefill layer: GEMM1 1.137 -> 1.102 ms, GEMM2 0.688 -> 0.640 ms; a
-    // streaming probe of the weight loads alone: 5.2 -> 6.2 TB/s).  It depends
-    // on (expert, tile) only, so every output keeps one K order.
-    const int rot = (e * 7 + tile * 13) % nst;
+    // (a streaming probe of the weight loads alone: 5.2 -> 6.2 TB/s).  The
+    // column tiles of one block, which share its token rows, start one stage
+    // apart: they then read each token line within a few stages of each other,
+    // which L2 holds, without all asking for the same lines at the same time.
+    // Prefill layer (GEMM1 / GEMM2 ms, HBM read bytes of GEMM1): no rotation
+    // 1.137 / 0.688, 3.58 GB; start keyed by expert only 1.11 / 0.68, 3.59 GB;
+    // by (expert, 13 x tile) 1.10 / 0.635, 5.0 GB; by (expert, tile) 1.068 /
+    // 0.623, 3.62 GB.  It depends on (expert, tile) only, so every output
+    // keeps one K order.
+    const int rot = (e * 7 + tile) % nst;
     auto kofs = [&](int st) -> uint32_t {
         const int k = st + rot;
         return uint32_t(k < nst ? k : k - nst) * kRowBytes;
