@@ -246,7 +246,8 @@ typedef struct moe_forward_args {
     void* out;            /* device bf16 [T, H] (output) */
     int32_t path;         /* MOE_PATH_*; AUTO unless a test forces a path */
     int32_t block_m;      /* rows per expert block; 0 lets the planner choose;
-                             small-M path: 16, 32 or 64; large-M path: 256 */
+                             small-M path: 16, 32 or 64; large-M path: 256
+                             (bf16) or 128 (fp8 and MXFP8) */
     int32_t flags;        /* MOE_FLAG_* bits; 0 is the layer of the pages' test */
     float clamp_limit;    /* SwiGLU clamp limit L: 0 for none, else L > 0
                              (+inf allowed, the same as none) */
@@ -317,10 +318,12 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  * Limits: bf16 requires H % 64 == 0 and I % 64 == 0; fp8 and MXFP8 require
  * H % 128 == 0 and I % 128 == 0; MXFP8 also T * H < 2^32 (else
  * MOE_ERR_UNSUPPORTED).  The large-M
- * path needs bf16 weights, H % 256 == 0 and I % 128 == 0; AUTO takes it from
- * 12 routed rows per expert (on average) on when min(E, T * topk) * I / 128 >=
- * 256, unless block_m names a size of the weight-streaming path (16, 32, 64);
- * forcing it elsewhere is MOE_ERR_UNSUPPORTED.
+ * path needs H % 256 == 0 and I % 128 == 0 (fp8 and MXFP8 also H, I <= 8192);
+ * it runs 256-row blocks for bf16 weights and 128-row blocks for fp8 and MXFP8
+ * weights.  AUTO takes it from 12 (bf16) or 48 (fp8, MXFP8) routed rows per
+ * expert (on average) on when min(E, T * topk) * I / 128 >= 256, unless
+ * block_m names a size of the weight-streaming path (16, 32, 64); forcing it
+ * elsewhere is MOE_ERR_UNSUPPORTED.
  * The workspace's activation scales (off_xs, off_inter_scale) are fp32 for
  * FP8_E4M3 and E8M0 bytes for MXFP8.  Unknown flag bits, and a clamp limit
  * that is negative or NaN, are MOE_ERR_INVALID_ARG.

@@ -252,8 +252,13 @@ hipError_t launch_gemm1_mx(const GemmArgs& g, hipStream_t s);   // MXFP8, block_
 hipError_t launch_gemm2_mx(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm1_large(const GemmArgs& g, bool fp8, hipStream_t s);
 hipError_t launch_gemm2_large(const GemmArgs& g, bool fp8, hipStream_t s);
-bool gemm_large_supported(int H, int I, bool fp8);   // shapes the LDS-tiled path handles
+bool gemm_large_supported(int H, int I, bool fp8);   // shapes the LDS-tiled bf16 path handles
 int gemm_large_block_m();                            // its rows per expert block
+// the LDS-tiled path for fp8 weights (128x128 block scales, or MXFP8)
+bool gemm_large_q_supported(int H, int I);
+int gemm_large_q_block_m();
+hipError_t launch_gemm1_large_q(const GemmArgs& g, bool mx, hipStream_t s);
+hipError_t launch_gemm2_large_q(const GemmArgs& g, bool mx, hipStream_t s);
 
 // The single-launch decode layer (fused.hip): block_m 16 and the shapes below.
 bool decode_layer_supported(int T, int topk, int H, int I, int block_m);

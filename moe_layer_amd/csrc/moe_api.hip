@@ -29,6 +29,11 @@ constexpr int kVersionMinor = 6;   // 1.1: MXFP8 weights; 1.2: layer variants; 1
 // CUs: on a layer as small as 8 experts, H 256, I 512 (16 rows per expert) the
 // tiled path's 32 workgroups took 0.037 ms against streaming's 0.025.
 constexpr double kLargeMinRowsPerExpert = 12.0;
+// fp8 and MXFP8 weights take their LDS-tiled path from this many rows per
+// expert (E 256, H 4096, I 256, layer ms, weight streaming vs tiled: fp8 at
+// 32 rows 0.320 vs 0.344, 64 rows 0.572 vs 0.454, 256 rows 1.77 vs 1.31;
+// MXFP8 0.321 vs 0.420, 0.577 vs 0.523, 1.79 vs 1.50)
+constexpr double kLargeQMinRowsPerExpert = 48.0;
 constexpr int64_t kLargeMinGemm1Tiles = 256;
 // From this many routed slots on, the alignment runs on many workgroups (one
 // workgroup's ALUs bound it above a few thousand slots).
@@ -62,7 +67,8 @@ int validate_forward_scalars(const moe_forward_args* a) {
     if ((a->flags & ~(MOE_FLAG_WEIGHT_ON_INPUT | MOE_FLAG_MX_PACKED_SCALES)) != 0) return MOE_ERR_INVALID_ARG;
     if ((a->flags & MOE_FLAG_MX_PACKED_SCALES) && a->wdtype != MOE_WDTYPE_MXFP8) return MOE_ERR_INVALID_ARG;
     if (!(a->clamp_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;   // negative or NaN
-    if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 256)
+    if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128 &&
+        a->block_m != 256)
         return MOE_ERR_UNSUPPORTED;
     const int q = a->wdtype == MOE_WDTYPE_BF16 ? 64 : MOE_QUANT_GROUP;
     if (a->H % q != 0 || a->I % q != 0) return MOE_ERR_UNSUPPORTED;
@@ -79,19 +85,20 @@ int make_plan(const moe_forward_args* a, Plan* p) {
     const bool fp8 = a->wdtype != MOE_WDTYPE_BF16;          // block-scaled fp8 or MXFP8
     const bool mx = a->wdtype == MOE_WDTYPE_MXFP8;
     const double rows_per_expert = double(R) / a->E;
-    const bool large_ok = gemm_large_supported(a->H, a->I, fp8);
+    const bool large_ok = fp8 ? gemm_large_q_supported(a->H, a->I) : gemm_large_supported(a->H, a->I, false);
+    const int large_bm = fp8 ? gemm_large_q_block_m() : gemm_large_block_m();
     int path = a->path;
     // AUTO with an explicit block size of the weight-streaming path stays on it
-    const bool bm_ok = a->block_m == 0 || a->block_m == gemm_large_block_m();
+    const bool bm_ok = a->block_m == 0 || a->block_m == large_bm;
     const bool wide = std::min<int64_t>(a->E, R) * (a->I / 128) >= kLargeMinGemm1Tiles;
+    const double min_rows = fp8 ? kLargeQMinRowsPerExpert : kLargeMinRowsPerExpert;
     if (path == MOE_PATH_AUTO)
-        path = (large_ok && bm_ok && wide && rows_per_expert >= kLargeMinRowsPerExpert) ? MOE_PATH_LARGE_M
-                                                                                        : MOE_PATH_SMALL_M;
+        path = (large_ok && bm_ok && wide && rows_per_expert >= min_rows) ? MOE_PATH_LARGE_M : MOE_PATH_SMALL_M;
     int bm = a->block_m;
     if (path == MOE_PATH_LARGE_M) {
         if (!large_ok) return MOE_ERR_UNSUPPORTED;
-        if (bm == 0) bm = gemm_large_block_m();
-        if (bm != gemm_large_block_m()) return MOE_ERR_UNSUPPORTED;
+        if (bm == 0) bm = large_bm;
+        if (bm != large_bm) return MOE_ERR_UNSUPPORTED;
     } else {
         if (bm == 0) bm = rows_per_expert <= 16.0 ? 16 : rows_per_expert <= 32.0 ? 32 : 64;
         if (bm > 64) return MOE_ERR_UNSUPPORTED;
@@ -344,12 +351,12 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
     }
     if ((st = mark(2)) != MOE_OK) return st;
     const bool large = p.path == MOE_PATH_LARGE_M;
-    const hipError_t g1 = large ? launch_gemm1_large(g, fp8, stream)
+    const hipError_t g1 = large ? (fp8 ? launch_gemm1_large_q(g, mx, stream) : launch_gemm1_large(g, false, stream))
                           : mx  ? launch_gemm1_mx(g, stream)
                                 : launch_gemm1_small(g, fp8, stream);
     if ((st = hip_status(g1)) != MOE_OK) return st;
     if ((st = mark(3)) != MOE_OK) return st;
-    const hipError_t g2 = large ? launch_gemm2_large(g, fp8, stream)
+    const hipError_t g2 = large ? (fp8 ? launch_gemm2_large_q(g, mx, stream) : launch_gemm2_large(g, false, stream))
                           : mx  ? launch_gemm2_mx(g, stream)
                                 : launch_gemm2_small(g, fp8, stream);
     if ((st = hip_status(g2)) != MOE_OK) return st;

@@ -81,7 +81,9 @@ def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAK
     (512, 64, 8, 0, 256, ops.MOE_PATH_LARGE_M),     # 64 rows per expert
     (4096, 128, 8, 0, 256, ops.MOE_PATH_LARGE_M),   # prefill: 256 rows per expert
     (1024, 256, 8, 2, 32, ops.MOE_PATH_SMALL_M),    # MXFP8: 32 rows per expert
-    (8192, 256, 8, 2, 64, ops.MOE_PATH_SMALL_M),    # MXFP8 has no large-M path
+    (8192, 256, 8, 2, 128, ops.MOE_PATH_LARGE_M),   # MXFP8: 256 rows per expert take the tiled path
+    (2048, 256, 8, 1, 128, ops.MOE_PATH_LARGE_M),   # fp8: 64 rows per expert
+    (1024, 256, 8, 2, 32, ops.MOE_PATH_SMALL_M),    # MXFP8: 32 rows per expert stream the weights
 ])
 def test_plan_block_size(T, E, k, wdtype, expect_bm, expect_path):
     H, I = (4096, 256) if wdtype else (4096, 1536)
@@ -117,9 +119,17 @@ def test_plan_block_override_and_path():
 def test_plan_large_path_limits():
     L = ops.lib()
     info = ops.PlanInfo()
-    # fp8 weights and H not a multiple of 256 have no large-M kernel
-    assert L.moe_plan(C.byref(_args(T=4096, wdtype=1, I=256, path=ops.MOE_PATH_LARGE_M)), C.byref(info)) \
-        == ops.MOE_ERR_UNSUPPORTED
+    # fp8 and MXFP8 weights take their own LDS-tiled kernels, on 128-row blocks
+    for wd in (1, 2):
+        p = ops.moe_plan(_args(T=4096, wdtype=wd, I=256, path=ops.MOE_PATH_LARGE_M))
+        assert p["path"] == ops.MOE_PATH_LARGE_M and p["block_m"] == 128
+        assert L.moe_plan(C.byref(_args(T=4096, wdtype=wd, I=256, path=ops.MOE_PATH_LARGE_M, block_m=256)),
+                          C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
+        assert L.moe_plan(C.byref(_args(T=4096, wdtype=wd, H=4224, I=256, path=ops.MOE_PATH_LARGE_M)),
+                          C.byref(info)) == ops.MOE_ERR_UNSUPPORTED      # H % 256 != 0
+        assert L.moe_plan(C.byref(_args(T=4096, wdtype=wd, H=8448, I=256, path=ops.MOE_PATH_LARGE_M)),
+                          C.byref(info)) == ops.MOE_ERR_UNSUPPORTED      # K beyond the scale table
+    # H not a multiple of 256 has no bf16 large-M kernel
     assert L.moe_plan(C.byref(_args(T=4096, H=4160, path=ops.MOE_PATH_LARGE_M)), C.byref(info)) \
         == ops.MOE_ERR_UNSUPPORTED
     assert L.moe_plan(C.byref(_args(path=ops.MOE_PATH_LARGE_M, block_m=64)), C.byref(info)) == ops.MOE_ERR_UNSUPPORTED
@@ -130,7 +140,7 @@ def test_plan_large_path_limits():
     assert p["path"] == ops.MOE_PATH_SMALL_M and p["block_m"] == 32
     # AUTO falls back to the weight-streaming path where the large one cannot run
     assert ops.moe_plan(_args(T=4096, H=4160))["path"] == ops.MOE_PATH_SMALL_M
-    assert ops.moe_plan(_args(T=8192, wdtype=1, I=256))["path"] == ops.MOE_PATH_SMALL_M
+    assert ops.moe_plan(_args(T=8192, wdtype=1, I=256, H=4224))["path"] == ops.MOE_PATH_SMALL_M
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -198,3 +198,14 @@ def test_intermediate_flip_rate_workloads(name):
     rate = bad / groups
     log(f"intermediate flip rate {name}: {bad} of {groups} {unit} differ ({rate:.2e}) over {nrows} rows")
     assert rate <= (2e-2 if cfg.wdtype == "bf16" else 0.25)
+
+
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("variant", ["plain", "clamp", "on_input", "both"])
+def test_intermediate_exact_q_lds_tiled(wdtype, variant):
+    """The fp8 / MXFP8 LDS-tiled GEMM1 (128-row blocks; operands dequantised
+    to bf16 in registers, block scales applied per 128-long K block): a hot
+    expert with several blocks, partly filled sub-tiles, odd token count."""
+    L = exact_layer(301, 5, 512, 384, 3, wdtype, pow2=variant in ("on_input", "both"), hot=2)
+    plan = _run_exact(L, ops.MOE_PATH_LARGE_M, 0, variant)
+    assert plan["path"] == ops.MOE_PATH_LARGE_M and plan["block_m"] == 128

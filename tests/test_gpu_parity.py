@@ -701,3 +701,92 @@ def test_decode_layer_max_experts_and_topk():
     alignment's limit), from logits."""
     from moe_layer_amd.workloads import Config
     _decode_layer_case(Config("dl_maxek", 4, 1024, 256, 128, 64, "bf16", "logits"))
+
+
+# ------------------------------------------- LDS-tiled fp8 / MXFP8 path ---
+
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("variant", ["plain", "on_input", "clamp", "both"])
+def test_forward_q_large_path_tiny(wdtype, variant):
+    """The fp8 and MXFP8 LDS-tiled kernels (128-row blocks) on the tiny layer,
+    plain and with the layer variants."""
+    kw = {} if variant == "plain" else _VARIANTS[variant]
+    cfg = replace(CONFIGS["tiny"], wdtype=wdtype)
+    a = ops.forward_args(None, None, None, None, None, shape=(cfg.T, cfg.E, cfg.H, cfg.I, cfg.topk,
+                                                               1 if wdtype == "fp8" else 2),
+                         path=ops.MOE_PATH_LARGE_M)
+    assert ops.moe_plan(a)["block_m"] == 128
+    _forward_case(cfg, path=ops.MOE_PATH_LARGE_M, **kw)
+
+
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
+def test_forward_q_large_path_ragged(wdtype):
+    """Odd token count, E not a power of two, a hot expert with several
+    128-row blocks, partly filled 32-row sub-tiles, invalid and duplicate ids,
+    K = H = 512 (4 stages) and I = 384 (3 stages: an odd stage count)."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config("ragged_q", 301, 5, 512, 384, 3, wdtype, "given")
+    wl = Workload(cfg)
+    rng = np.random.default_rng(16)
+    ids = rng.integers(0, 5, size=(301, 3)).astype(np.int32)
+    ids[0, 1] = ids[0, 0]
+    ids[1, 2] = -1
+    ids[2, 0] = 5
+    ids[10:250, 0] = 3
+    tw = rng.random((301, 3)).astype(np.float32)
+    layer = layer_for(cfg)
+    layer.ensure(range(5))
+    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_LARGE_M)
+    gpu = out.to(torch.float64).cpu().numpy()
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(301))
+    excess, raw, _ = compare_output(gpu, o)
+    log(f"ragged large {wdtype}: excess/RMS={excess:.3e} raw={raw:.3e}")
+    assert np.all(np.isfinite(gpu))
+    assert excess <= TAU[wdtype]
+
+
+@pytest.mark.parametrize("name", ["fp8", "mxfp8"])
+def test_forward_q_large_path_workload(name):
+    """The 1024-token fp8 / MXFP8 layer (32 rows per expert) on the tiled path,
+    every token against the oracle."""
+    _forward_case(CONFIGS[name], path=ops.MOE_PATH_LARGE_M)
+
+
+@pytest.mark.parametrize("name", ["fp8", "mxfp8"])
+def test_forward_q_large_path_8192_tokens_sampled(name):
+    """8192 tokens of the fp8 / MXFP8 layer (256 rows per expert: two 128-row
+    blocks each) on the tiled path, sampled tokens against the oracle."""
+    rng = np.random.default_rng(21)
+    _forward_case(CONFIGS[name].with_tokens(8192), tokens=np.sort(rng.choice(8192, 96, replace=False)),
+                  path=ops.MOE_PATH_LARGE_M)
+
+
+def test_forward_q_large_path_mx_packed_scales_bitwise():
+    """The MXFP8 tiled kernels read packed weight scales to the same bits as
+    row-major ones."""
+    cfg = CONFIGS["mxfp8"].with_tokens(256)
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    ref, _, (x, ids_t, tw_t) = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_LARGE_M)
+    s13p, s2p = ops.moe_pack_mx_scales(layer.s13), ops.moe_pack_mx_scales(layer.s2)
+    out, _ = ops.moe_forward(x, layer.w13, layer.w2, ids_t, tw_t, s13p, s2p, path=ops.MOE_PATH_LARGE_M,
+                             mx_packed_scales=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("name", ["fp8", "mxfp8"])
+def test_q_large_path_determinism_and_permutation(name):
+    """Two runs agree bitwise (the second on an 0xFF-poisoned workspace), and a
+    token permutation permutes the output."""
+    cfg = CONFIGS[name].with_tokens(512)
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    x = wl.x_bf16_bits()
+    out1, ws, (xt, ids_t, tw_t) = run_forward(layer, x, ids, tw, path=ops.MOE_PATH_LARGE_M)
+    ws.fill_(0xFF)
+    out2, _ = ops.moe_forward(xt, layer.w13, layer.w2, ids_t, tw_t, layer.s13, layer.s2, workspace=ws,
+                              path=ops.MOE_PATH_LARGE_M)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    p = np.random.default_rng(4).permutation(cfg.T)
+    outp, _, _ = run_forward(layer, x[p], ids[p], tw[p], path=ops.MOE_PATH_LARGE_M)
+    assert torch.equal(outp, out1[torch.from_numpy(p).to(out1.device)])
