@@ -76,6 +76,7 @@ def parse():
 # valid only while these are unchanged)
 KERNEL_SOURCES = {"small": ("gemm_small.hip", "dev_gemm_small.h", "common.h"),
                   "large": ("gemm_large.hip", "common.h"),
+                  "large_q": ("gemm_large_q.hip", "common.h"),
                   "mx": ("gemm_mx.hip", "dev_gemm_mx.h", "common.h")}
 
 
@@ -301,9 +302,12 @@ def measure(args, workload, tokens, steps, warmup, with_cpu, copy_calibration):
         roof = {"bound": "mfma", "achieved": round(g1_tfs, 2), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(g1_tfs / peak_tf, 4)}
     large = plan["path"] == 2
-    digest = kernel_source_digest("large" if large else "mx" if mx else "small")
+    fp8w = cfg.wdtype != "bf16"
+    digest = kernel_source_digest(("large_q" if fp8w else "large") if large else "mx" if mx else "small")
     roof["traffic"] = read_traffic(cfg.name if not tokens else f"{cfg.name}@{T}", digest)
-    roof["kernel"] = ("gemm_large_kernel<1> (LDS-tiled GEMM1 + SiLU-mul epilogue)" if large
+    roof["kernel"] = ("gemm_large_q_kernel<1> (LDS-tiled fp8/MXFP8 GEMM1 + SiLU-mul-quant epilogue)"
+                      if large and fp8w
+                      else "gemm_large_kernel<1> (LDS-tiled GEMM1 + SiLU-mul epilogue)" if large
                       else "gemm1_mx_kernel (weight-streaming MXFP8 GEMM1 + SiLU-mul-quant epilogue)" if mx
                       else "gemm1_small_kernel (weight-streaming GEMM1 + SiLU-mul epilogue)")
     roof["kernel_ms"] = round(float(g1_ms), 5)

@@ -320,8 +320,8 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  * MOE_ERR_UNSUPPORTED).  The large-M
  * path needs H % 256 == 0 and I % 128 == 0 (fp8 and MXFP8 also H, I <= 8192);
  * it runs 256-row blocks for bf16 weights and 128-row blocks for fp8 and MXFP8
- * weights.  AUTO takes it from 12 (bf16) or 48 (fp8, MXFP8) routed rows per
- * expert (on average) on when min(E, T * topk) * I / 128 >= 256, unless
+ * weights.  AUTO takes it from 12 (bf16), 20 (fp8) or 28 (MXFP8) routed rows
+ * per expert (on average) on when min(E, T * topk) * I / 128 >= 256, unless
  * block_m names a size of the weight-streaming path (16, 32, 64); forcing it
  * elsewhere is MOE_ERR_UNSUPPORTED.
  * The workspace's activation scales (off_xs, off_inter_scale) are fp32 for

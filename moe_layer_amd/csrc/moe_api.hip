@@ -31,9 +31,11 @@ constexpr int kVersionMinor = 6;   // 1.1: MXFP8 weights; 1.2: layer variants; 1
 constexpr double kLargeMinRowsPerExpert = 12.0;
 // fp8 and MXFP8 weights take their LDS-tiled path from this many rows per
 // expert (E 256, H 4096, I 256, layer ms, weight streaming vs tiled: fp8 at
-// 32 rows 0.320 vs 0.344, 64 rows 0.572 vs 0.454, 256 rows 1.77 vs 1.31;
-// MXFP8 0.321 vs 0.420, 0.577 vs 0.523, 1.79 vs 1.50)
-constexpr double kLargeQMinRowsPerExpert = 48.0;
+// 8 rows 0.196 vs 0.229, 16 rows 0.250 vs 0.257, 24 rows 0.297 vs 0.286, 32
+// rows 0.317 vs 0.305, 256 rows 1.77 vs 1.16; MXFP8 0.200 vs 0.240, 0.259 vs
+// 0.260, 0.283 vs 0.287, 0.323 vs 0.305, 1.78 vs 1.15)
+constexpr double kLargeQMinRowsPerExpert = 20.0;
+constexpr double kLargeMxMinRowsPerExpert = 28.0;
 constexpr int64_t kLargeMinGemm1Tiles = 256;
 // From this many routed slots on, the alignment runs on many workgroups (one
 // workgroup's ALUs bound it above a few thousand slots).
@@ -91,7 +93,8 @@ int make_plan(const moe_forward_args* a, Plan* p) {
     // AUTO with an explicit block size of the weight-streaming path stays on it
     const bool bm_ok = a->block_m == 0 || a->block_m == large_bm;
     const bool wide = std::min<int64_t>(a->E, R) * (a->I / 128) >= kLargeMinGemm1Tiles;
-    const double min_rows = fp8 ? kLargeQMinRowsPerExpert : kLargeMinRowsPerExpert;
+    const double min_rows = !fp8 ? kLargeMinRowsPerExpert
+                            : a->wdtype == MOE_WDTYPE_MXFP8 ? kLargeMxMinRowsPerExpert : kLargeQMinRowsPerExpert;
     if (path == MOE_PATH_AUTO)
         path = (large_ok && bm_ok && wide && rows_per_expert >= min_rows) ? MOE_PATH_LARGE_M : MOE_PATH_SMALL_M;
     int bm = a->block_m;

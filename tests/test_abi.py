@@ -73,17 +73,20 @@ def _args(T=16, E=128, H=4096, I=1536, k=8, wdtype=0, path=0, block_m=0, ptr=FAK
 
 @pytest.mark.parametrize("T,E,k,wdtype,expect_bm,expect_path", [
     (16, 128, 8, 0, 16, ops.MOE_PATH_SMALL_M),      # decode: 1 row per expert
-    (1024, 256, 8, 1, 32, ops.MOE_PATH_SMALL_M),    # fp8: 32 rows per expert
+    (1024, 256, 8, 1, 128, ops.MOE_PATH_LARGE_M),   # fp8: 32 rows per expert take the tiled path
+    (512, 256, 8, 1, 16, ops.MOE_PATH_SMALL_M),     # fp8: 16 rows per expert stream the weights
+    (640, 256, 8, 1, 128, ops.MOE_PATH_LARGE_M),    # fp8: 20 rows per expert
     (128, 128, 8, 0, 16, ops.MOE_PATH_SMALL_M),     # 8 rows per expert: weight streaming
     (176, 128, 8, 0, 16, ops.MOE_PATH_SMALL_M),     # 11 rows per expert
     (192, 128, 8, 0, 256, ops.MOE_PATH_LARGE_M),    # 12 rows per expert: LDS-tiled from here on
     (64, 8, 2, 0, 16, ops.MOE_PATH_SMALL_M),        # tiny: 16 rows per expert, too few tiles for the LDS path
     (512, 64, 8, 0, 256, ops.MOE_PATH_LARGE_M),     # 64 rows per expert
     (4096, 128, 8, 0, 256, ops.MOE_PATH_LARGE_M),   # prefill: 256 rows per expert
-    (1024, 256, 8, 2, 32, ops.MOE_PATH_SMALL_M),    # MXFP8: 32 rows per expert
-    (8192, 256, 8, 2, 128, ops.MOE_PATH_LARGE_M),   # MXFP8: 256 rows per expert take the tiled path
+    (1024, 256, 8, 2, 128, ops.MOE_PATH_LARGE_M),   # MXFP8: 32 rows per expert
+    (8192, 256, 8, 2, 128, ops.MOE_PATH_LARGE_M),   # MXFP8: 256 rows per expert
     (2048, 256, 8, 1, 128, ops.MOE_PATH_LARGE_M),   # fp8: 64 rows per expert
-    (1024, 256, 8, 2, 32, ops.MOE_PATH_SMALL_M),    # MXFP8: 32 rows per expert stream the weights
+    (768, 256, 8, 2, 32, ops.MOE_PATH_SMALL_M),     # MXFP8: 24 rows per expert stream the weights
+    (896, 256, 8, 2, 128, ops.MOE_PATH_LARGE_M),    # MXFP8: 28 rows per expert
 ])
 def test_plan_block_size(T, E, k, wdtype, expect_bm, expect_path):
     H, I = (4096, 256) if wdtype else (4096, 1536)

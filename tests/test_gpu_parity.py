@@ -720,12 +720,18 @@ def test_forward_q_large_path_tiny(wdtype, variant):
 
 
 @pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
-def test_forward_q_large_path_ragged(wdtype):
+@pytest.mark.parametrize("H,I,variant", [(512, 384, "plain"), (512, 256, "plain"), (768, 128, "plain"),
+                                         (512, 256, "both"), (768, 256, "clamp"), (768, 128, "on_input")])
+def test_forward_q_large_path_ragged(wdtype, H, I, variant):
     """Odd token count, E not a power of two, a hot expert with several
     128-row blocks, partly filled 32-row sub-tiles, invalid and duplicate ids,
-    K = H = 512 (4 stages) and I = 384 (3 stages: an odd stage count)."""
+    K = H = 512 (4 stages) and I = 384 (3 stages: an odd stage count).  With
+    I <= 256 the down GEMM keeps the token tile in LDS and walks several
+    column tiles per workgroup: H = 512 gives two tiles per workgroup, H = 768
+    (three tiles) one, and I = 128 a single K stage per tile."""
     from moe_layer_amd.workloads import Config
-    cfg = Config("ragged_q", 301, 5, 512, 384, 3, wdtype, "given")
+    kw = {} if variant == "plain" else _VARIANTS[variant]
+    cfg = Config("ragged_q", 301, 5, H, I, 3, wdtype, "given")
     wl = Workload(cfg)
     rng = np.random.default_rng(16)
     ids = rng.integers(0, 5, size=(301, 3)).astype(np.int32)
@@ -736,11 +742,13 @@ def test_forward_q_large_path_ragged(wdtype):
     tw = rng.random((301, 3)).astype(np.float32)
     layer = layer_for(cfg)
     layer.ensure(range(5))
-    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_LARGE_M)
+    out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, path=ops.MOE_PATH_LARGE_M, **kw)
     gpu = out.to(torch.float64).cpu().numpy()
-    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(301))
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(301),
+                      weight_on_input=kw.get("weight_on_input", False),
+                      clamp_limit=kw.get("clamp_limit", 0.0))
     excess, raw, _ = compare_output(gpu, o)
-    log(f"ragged large {wdtype}: excess/RMS={excess:.3e} raw={raw:.3e}")
+    log(f"ragged large {wdtype} H={H} I={I} {variant}: excess/RMS={excess:.3e} raw={raw:.3e}")
     assert np.all(np.isfinite(gpu))
     assert excess <= TAU[wdtype]
 
