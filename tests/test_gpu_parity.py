@@ -721,14 +721,16 @@ def test_forward_q_large_path_tiny(wdtype, variant):
 
 @pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
 @pytest.mark.parametrize("H,I,variant", [(512, 384, "plain"), (512, 256, "plain"), (768, 128, "plain"),
-                                         (512, 256, "both"), (768, 256, "clamp"), (768, 128, "on_input")])
+                                         (512, 256, "both"), (768, 256, "clamp"), (768, 128, "on_input"),
+                                         (4352, 256, "plain")])
 def test_forward_q_large_path_ragged(wdtype, H, I, variant):
     """Odd token count, E not a power of two, a hot expert with several
     128-row blocks, partly filled 32-row sub-tiles, invalid and duplicate ids,
     K = H = 512 (4 stages) and I = 384 (3 stages: an odd stage count).  With
     I <= 256 the down GEMM keeps the token tile in LDS and walks several
     column tiles per workgroup: H = 512 gives two tiles per workgroup, H = 768
-    (three tiles) one, and I = 128 a single K stage per tile."""
+    (three tiles) one, H = 4352 (17 tiles) one, and I = 128 a single K stage
+    per tile."""
     from moe_layer_amd.workloads import Config
     kw = {} if variant == "plain" else _VARIANTS[variant]
     cfg = Config("ragged_q", 301, 5, H, I, 3, wdtype, "given")
