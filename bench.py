@@ -344,7 +344,7 @@ def measure(args, workload, tokens, steps, warmup, with_cpu, copy_calibration):
         "config": {"workload": f"{cfg.name} MoE layer T={T} E={E} H={H} I={I} topk={k} {cfg.wdtype}",
                    "T": T, "E": E, "H": H, "I": I, "topk": k, "weights": cfg.wdtype,
                    "block_m": plan["block_m"], "path": ["auto", "small_m", "large_m"][plan["path"]],
-                   "gemm1_mfma": "bf16", "gemm2_mfma": cfg.wdtype,
+                   "gemm1_mfma": "bf16", "gemm2_mfma": "bf16" if plan["path"] == 2 else cfg.wdtype,
                    "launch": "one decode-layer kernel" if use_dl else "one kernel per stage",
                    **({"mx_scales": "packed" if packed else "row-major"} if mx else {}),
                    "parallelism": "single GPU"},

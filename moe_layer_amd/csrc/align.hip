@@ -38,6 +38,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restri
                                                         int32_t* __restrict__ inv) {
     __shared__ int cnt[kWaves * kMaxE];   // counts, then running start positions
     __shared__ int offs[kMaxE + 1];       // exclusive scan of padded sizes
+    __shared__ int pstart[kMaxE];         // first padding slot of each expert
     __shared__ int wsum[kWaves];
 
     const int tid = threadIdx.x;
@@ -111,10 +112,14 @@ __global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restri
             cnt[ww * E + tid] = run;
             run += c;
         }
-        for (int p = run; p < offs[tid + 1]; ++p) sorted[p] = R;   // padding of expert tid
+        pstart[tid] = run;
     }
     if (tid == 0) ntpp[0] = offs[E];
     __syncthreads();
+    // padding: one wave per expert, consecutive lanes on consecutive slots (a
+    // thread per expert writing its own run made every store touch 64 lines)
+    for (int ee = w; ee < E; ee += kWaves)
+        for (int p = pstart[ee] + lane; p < offs[ee + 1]; p += 64) sorted[p] = R;
 
     // ---- phase 3: stable scatter ---------------------------------------------
     for (int base = begin; base < end; base += 64 * kBatchUnroll) {
@@ -244,6 +249,7 @@ __global__ __launch_bounds__(kThreads) void align_scan_kernel(const int32_t* __r
                                                               int32_t* __restrict__ ntpp) {
     __shared__ int part_sum[kThreads];
     __shared__ int offs[kMaxE + 1];
+    __shared__ int pstart[kMaxE];
     __shared__ int wsum[kWaves];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     int ep = 1;
@@ -306,8 +312,16 @@ __global__ __launch_bounds__(kThreads) void align_scan_kernel(const int32_t* __r
             starts[i] = run;
             run += counts[i];
         }
-        for (int p = beg + filled + part; p < end; p += parts) sorted[p] = R;               // padding
-        for (int b = beg / B + part; b < end / B; b += parts) expert_ids[b] = e;             // its blocks
+        if (part == 0) pstart[e] = beg + filled;
+    }
+    __syncthreads();
+    // padding and block experts: one wave per expert, consecutive lanes on
+    // consecutive slots (threads of different experts made every store touch
+    // 64 lines: 17.5 us for the fp8 layer's 256 experts)
+    for (int ee = w; ee < E; ee += kWaves) {
+        const int beg = offs[ee], end = offs[ee + 1];
+        for (int p = pstart[ee] + lane; p < end; p += 64) sorted[p] = R;
+        for (int b = beg / B + lane; b < end / B; b += 64) expert_ids[b] = ee;
     }
     const int all = offs[E];
     if (tid == 0) ntpp[0] = all;
