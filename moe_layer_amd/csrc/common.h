@@ -39,6 +39,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16_rne(f)); }
 
+// The down GEMM's per-slot rows y: fp32 for layers with bf16 weights, bf16
+// (round to nearest even) for fp8 and MXFP8 weights, whose e4m3 intermediate
+// already carries a relative error of up to 2^-4 against bf16 y's 2^-9: it
+// halves the y round trip between the down GEMM and the combine.
+template <bool kBf16Y>
+__device__ __forceinline__ void store_y4(float* y, int64_t idx, const f32x4& v) {
+    if constexpr (kBf16Y) {
+        uint2 p;
+        p.x = uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
+        p.y = uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + idx) = p;
+    } else {
+        *reinterpret_cast<f32x4*>(y + idx) = v;
+    }
+}
+
 // fp32 -> OCP E4M3FN byte, round to nearest even.  The input must be finite
 // and within [-448, 448] (callers clamp first).  E4M3FN: exponent bias 7,
 // 3 fraction bits, subnormal quantum 2^-9 below 2^-6.
@@ -183,7 +199,7 @@ struct GemmArgs {
     const int32_t* ntpp;        // [1]
     void* inter;                // bf16 or fp8 [cap, I]
     float* inter_scale;         // fp32 [cap, I/128] (fp8) or E8M0 bytes [cap, I/32] (MXFP8)
-    float* y;                   // fp32 [T*topk, H]
+    float* y;                   // [T*topk, H]: fp32 (bf16 weights) or bf16 (fp8, MXFP8 weights; store_y4)
     int weight_on_input;        // router weight on GEMM1's input instead of GEMM2's output
     int mx_packed;              // MXFP8 weight scales in the tile-packed layout (moe_pack_mx_scales)
     int krot;                   // the fp8 GEMM1 walks K from a per-(expert, column tile) start (k_rotation)
@@ -267,7 +283,7 @@ hipError_t launch_decode_layer(const GemmArgs& g, int wdtype_fp8, int mx, const 
                                int32_t* expert_ids, int32_t* ntpp, int cap, uint8_t* xq, void* xs, uint16_t* out,
                                uint32_t* sync, hipStream_t s);
 
-hipError_t launch_combine(const float* y, const int32_t* ids, int T, int topk, int E, int H,
+hipError_t launch_combine(const float* y, bool bf16_y, const int32_t* ids, int T, int topk, int E, int H,
                           uint16_t* out, hipStream_t s);
 
 }  // namespace moe

@@ -360,7 +360,7 @@ __device__ __forceinline__ void gemm2_mx_tile(const GemmArgs& g, int blk, int ti
             f32x4 v;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = __fmul_rn(acc[m][n][j], tw);
-            *reinterpret_cast<f32x4*>(g.y + int64_t(f) * H + col) = v;
+            store_y4<true>(g.y, int64_t(f) * H + col, v);
         }
     }
 }
@@ -458,7 +458,7 @@ __device__ __forceinline__ void gemm2_mx_tiles(const GemmArgs& g, int blk, int t
                 f32x4 o;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o[j] = __fmul_rn(acc[m][n][j], tw[n]);
-                *reinterpret_cast<f32x4*>(g.y + int64_t(f[n]) * H + hc + m * 16 + 4 * lk) = o;
+                store_y4<true>(g.y, int64_t(f[n]) * H + hc + m * 16 + 4 * lk, o);
             }
         }
         clear();

@@ -440,7 +440,7 @@ __device__ __forceinline__ void gemm2_small_tile(const GemmArgs& g, int blk, int
             f32x4 v;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = __fmul_rn(acc[m][n][j], tw);
-            *reinterpret_cast<f32x4*>(g.y + int64_t(f) * H + col) = v;
+            store_y4<FP8>(g.y, int64_t(f) * H + col, v);
         }
     }
 }
@@ -553,7 +553,7 @@ __device__ __forceinline__ void gemm2_tiles(const GemmArgs& g, int blk, int tile
                 f32x4 o;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o[j] = __fmul_rn(acc[m][n][j], tw[n]);
-                *reinterpret_cast<f32x4*>(g.y + int64_t(f[n]) * H + hc + m * 16 + 4 * lk) = o;
+                store_y4<FP8>(g.y, int64_t(f[n]) * H + hc + m * 16 + 4 * lk, o);
             }
         }
         clear();

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(FusedArgs a) {
     for (int64_t i = int64_t(wg) * kThreads + threadIdx.x; i < int64_t(g.T) * per_row;
          i += int64_t(nwg) * kThreads) {
         const int t = int(i / per_row);
-        combine_chunk(g.y, a.ids, g.topk, g.E, g.H, a.out, t, int(i - int64_t(t) * per_row) * 8);
+        combine_chunk<(W > 0)>(g.y, a.ids, g.topk, g.E, g.H, a.out, t, int(i - int64_t(t) * per_row) * 8);
     }
     grid_exit(a.sync, nwg);
 }

@@ -41,7 +41,7 @@
 //                  scale of its 128-column group (amax across the four waves
 //                  through LDS) or of each 32-column group (one wave's
 //                  columns), and e4m3 codes (P2 sections 1.1, 1.2).
-//   GEMM2 (a6):    tile = 256 output columns h; epilogue y[f] = tw[f] * acc.
+//   GEMM2 (a6):    tile = 256 output columns h; epilogue y[f] = bf16(tw[f] * acc).
 #include "common.h"
 
 namespace moe {
@@ -421,7 +421,7 @@ __device__ __forceinline__ void run_tile_q(const GemmArgs& g, const RingQ& ring,
             const int f = g.sorted_ids[blk * kBM + (2 * u + grp) * 32 + fr];
             if (f >= R) continue;
             const float tw = gemm2_row_weight(g, f);
-            float* yrow = g.y + int64_t(f) * g.H;
+            const int64_t yrow = int64_t(f) * g.H;
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -429,7 +429,7 @@ __device__ __forceinline__ void run_tile_q(const GemmArgs& g, const RingQ& ring,
                     f32x4 v;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = __fmul_rn(acc[a][u][q * 4 + j], tw);
-                    *reinterpret_cast<f32x4*>(yrow + hw + a * 32 + q * 8 + fk * 4) = v;
+                    store_y4<true>(g.y, yrow + hw + a * 32 + q * 8 + fk * 4, v);
                 }
         }
     }
@@ -694,7 +694,7 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 if (fo[u] < R) {
-                    float* yrow = g.y + int64_t(fo[u]) * g.H;
+                    const int64_t yrow = int64_t(fo[u]) * g.H;
 #pragma unroll
                     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -702,7 +702,7 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
                             f32x4 v;
 #pragma unroll
                             for (int j = 0; j < 4; ++j) v[j] = __fmul_rn(acc[a][u][q * 4 + j], two[u]);
-                            *reinterpret_cast<f32x4*>(yrow + hw + a * 32 + q * 8 + fk * 4) = v;
+                            store_y4<true>(g.y, yrow + hw + a * 32 + q * 8 + fk * 4, v);
                         }
                 }
 #pragma unroll

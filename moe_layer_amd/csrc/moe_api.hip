@@ -132,8 +132,9 @@ int make_plan(const moe_forward_args* a, Plan* p) {
     p->off_inter_scale = mx    ? take(rows * (a->I / MOE_MX_BLOCK))
                          : fp8 ? take(rows * (a->I / MOE_QUANT_GROUP) * 4)
                                : -1;
-    // y also serves as the wide alignment's scratch (used before GEMM2 writes y)
-    p->off_y = take(std::max(R * a->H * 4, align_scratch_bytes(R, a->E)));
+    // y (fp32, or bf16 for fp8 and MXFP8 weights) also serves as the wide
+    // alignment's scratch (used before GEMM2 writes y)
+    p->off_y = take(std::max(R * a->H * (fp8 ? 2 : 4), align_scratch_bytes(R, a->E)));
     p->total = off;
     return MOE_OK;
 }
@@ -364,7 +365,7 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
                                 : launch_gemm2_small(g, fp8, stream);
     if ((st = hip_status(g2)) != MOE_OK) return st;
     if ((st = mark(4)) != MOE_OK) return st;
-    if ((st = hip_status(launch_combine(g.y, a->topk_ids, a->T, a->topk, a->E, a->H,
+    if ((st = hip_status(launch_combine(g.y, fp8, a->topk_ids, a->T, a->topk, a->E, a->H,
                                         static_cast<uint16_t*>(a->out), stream))) != MOE_OK)
         return st;
     return mark(5);

@@ -55,7 +55,8 @@ static void check_plan(const moe_forward_args& a) {
         else CHECK(o % 256 == 0 && o >= prev && o <= p.workspace_bytes);
         prev = o;
     }
-    CHECK(p.off_y + int64_t(a.T) * a.topk * a.H * 4 <= p.workspace_bytes);
+    // y: bf16 for fp8 and MXFP8 weights, fp32 for bf16 weights
+    CHECK(p.off_y + int64_t(a.T) * a.topk * a.H * (a.wdtype == MOE_WDTYPE_BF16 ? 4 : 2) <= p.workspace_bytes);
     // a too-small workspace is rejected before any launch
     if (a.T > 0) {
         const int st2 = moe_forward(&a, fake(), p.workspace_bytes - 1, nullptr);
