@@ -140,7 +140,7 @@ MOE_API int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t 
 
 /*
  * moe_align_scratch_bytes — device scratch bytes moe_align_ws needs for
- * T * topk routed slots over E experts: 0 below 2048 slots (one workgroup
+ * T * topk routed slots over E experts: 0 up to 8192 slots (one workgroup
  * aligns them, as moe_align does), else the per-workgroup expert counts and
  * starts of the multi-workgroup form (2 * ceil(T*topk / 1024) * E int32,
  * rounded up to 256 bytes).  Host only; negative status on invalid arguments.
@@ -149,13 +149,13 @@ MOE_API int64_t moe_align_scratch_bytes(int32_t T, int32_t topk, int32_t E);
 
 /*
  * moe_align_ws — moe_align (same definition, same outputs bit for bit) on
- * many workgroups: from 2048 routed slots on, one workgroup per 1024 slots
+ * many workgroups: above 8192 routed slots, one workgroup per 1024 slots
  * counts its slots per expert, one workgroup scans the counts into padded
  * expert offsets and per-workgroup starts, and the counting workgroups
  * scatter their slots (stable: ascending flat index within an expert).
- * Below 2048 slots it is moe_align.  One workgroup's ALUs bound moe_align
- * above a few thousand slots (the prefill layer's 32768 slots: 63 against
- * 27 us for the multi-workgroup form).
+ * Up to 8192 slots it is moe_align.  One workgroup's ALUs bound moe_align
+ * above that (16384 slots: 35 against 27 us; the prefill layer's 32768
+ * slots: 63 against 27 us for the multi-workgroup form).
  *
  *   scratch        device, >= moe_align_scratch_bytes(T, topk, E) bytes,
  *                  4-byte aligned (may be NULL when that is 0); contents on

@@ -37,9 +37,11 @@ constexpr double kLargeMinRowsPerExpert = 12.0;
 constexpr double kLargeQMinRowsPerExpert = 20.0;
 constexpr double kLargeMxMinRowsPerExpert = 28.0;
 constexpr int64_t kLargeMinGemm1Tiles = 256;
-// From this many routed slots on, the alignment runs on many workgroups (one
-// workgroup's ALUs bound it above a few thousand slots).
-constexpr int64_t kAlignWideMinSlots = 2048;
+// Above 8192 routed slots the alignment runs on many workgroups (one
+// workgroup's ALUs bound it beyond; align stage us, one workgroup vs many:
+// 2048 slots 14.6 vs 24.3, 4096 14.8 vs 23.8, 8192 21.9 vs 25.5, 16384 35.3
+// vs 27.0, 32768 63 vs 27).
+constexpr int64_t kAlignWideMinSlots = 8193;
 // The fp8 GEMM1 walks K from a per-(expert, tile) start up to this many
 // routed rows per expert (k_rotation; fp8 layer: 64 tokens 127 -> 94 us, 256
 // tokens 154 -> 109 us, 512 tokens 143 -> 138 us; the MXFP8 GEMM1 always does).

@@ -168,7 +168,7 @@ def moe_align_scratch_bytes(T: int, topk: int, E: int) -> int:
 
 
 def moe_align_ws(topk_ids: torch.Tensor, E: int, block_m: int, with_inv: bool = True, scratch=None):
-    """moe_align on many workgroups (from 2048 routed slots; the same outputs)."""
+    """moe_align on many workgroups (above 8192 routed slots; the same outputs)."""
     assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous() and topk_ids.dim() == 2
     T, k = topk_ids.shape
     cap = moe_align_capacity(T, k, E, block_m)

@@ -85,7 +85,7 @@ def test_align_workloads(name, B):
 @pytest.mark.parametrize("T,k,E,B", [(100, 8, 64, 16), (256, 8, 64, 16), (4096, 8, 128, 64), (4096, 8, 128, 256),
                                      (8192, 8, 256, 16), (3000, 3, 5, 16), (2000, 64, 40, 7), (999, 5, 1024, 16)])
 def test_align_ws_multi_workgroup(T, k, E, B):
-    """moe_align_ws (many workgroups from 2048 slots on, one below) gives the
+    """moe_align_ws (many workgroups above 8192 slots, one up to it) gives the
     oracle's alignment bit for bit, inverse permutation included, also on a
     scratch buffer poisoned with 0xFF bytes."""
     rng = np.random.default_rng(T * 7 + E + B)
@@ -110,8 +110,8 @@ def test_align_empty_experts_worked_example():
                                      (1000, 7, 1024, 64), (4096, 8, 128, 256), (8192, 8, 256, 256),
                                      (3000, 3, 5, 16)])
 def test_forward_alignment_buffers(T, k, E, B):
-    """The alignment moe_forward leaves in its workspace (one workgroup below
-    2048 slots, several above) equals the oracle's, bit for bit."""
+    """The alignment moe_forward leaves in its workspace (one workgroup up to
+    8192 slots, several above) equals the oracle's, bit for bit."""
     from moe_layer_amd.workloads import Config
     cfg = Config("align", T, E, 256, 128, k, "bf16", "given")
     layer = layer_for(cfg)
