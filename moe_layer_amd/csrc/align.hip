@@ -20,6 +20,7 @@
 //                        Used when the slot count is large enough that one
 //                        CU's ALUs would be the bottleneck.
 #include "dev_align.h"
+#include "dev_quant.h"
 
 namespace moe {
 
@@ -30,12 +31,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBatchUnroll = 4;   // batches whose loads are issued together
 
 
-__global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restrict__ ids, int R,
-                                                        int E, int B, int cap,
-                                                        int32_t* __restrict__ sorted,
-                                                        int32_t* __restrict__ expert_ids,
-                                                        int32_t* __restrict__ ntpp,
-                                                        int32_t* __restrict__ inv) {
+__device__ __forceinline__ void align_one_wg(const int32_t* __restrict__ ids, int R, int E, int B, int cap,
+                                             int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
+                                             int32_t* __restrict__ ntpp, int32_t* __restrict__ inv) {
     __shared__ int cnt[kWaves * kMaxE];   // counts, then running start positions
     __shared__ int offs[kMaxE + 1];       // exclusive scan of padded sizes
     __shared__ int pstart[kMaxE];         // first padding slot of each expert
@@ -163,6 +161,50 @@ __global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restri
             e = lo - 1;
         }
         expert_ids[b] = e;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void align_kernel(const int32_t* __restrict__ ids, int R,
+                                                        int E, int B, int cap,
+                                                        int32_t* __restrict__ sorted,
+                                                        int32_t* __restrict__ expert_ids,
+                                                        int32_t* __restrict__ ntpp,
+                                                        int32_t* __restrict__ inv) {
+    align_one_wg(ids, R, E, B, cap, sorted, expert_ids, ntpp, inv);
+}
+
+// The one-workgroup alignment and the layer input's fp8 quantisation in one
+// launch: workgroup 0 aligns (on one CU), the others quantise x in a
+// grid-stride loop (16 lanes per 128-column group, or 4 per 32-column MXFP8
+// group), so the quantisation runs beside the alignment instead of after it.
+// Up to kTinyMaxSlots slots workgroup 0 runs the one-wave alignment.
+template <bool MX, bool TINY>
+__global__ __launch_bounds__(kThreads) void align_quant_kernel(const int32_t* __restrict__ ids, int R, int E, int B,
+                                                              int cap, int32_t* __restrict__ sorted,
+                                                              int32_t* __restrict__ expert_ids,
+                                                              int32_t* __restrict__ ntpp,
+                                                              const uint16_t* __restrict__ x, int T, int H,
+                                                              uint8_t* __restrict__ xq, void* __restrict__ xs) {
+    if (blockIdx.x == 0) {
+        if constexpr (TINY) {
+            __shared__ int cnt[kMaxE];
+            __shared__ int offs[kMaxE + 1];
+            align_tiny_wg<kTinyBatches>(ids, R, E, B, cap, sorted, expert_ids, ntpp, nullptr, cnt, offs,
+                                        threadIdx.x < 64);
+        } else {
+            align_one_wg(ids, R, E, B, cap, sorted, expert_ids, ntpp, nullptr);
+        }
+        return;
+    }
+    constexpr int kLanes = MX ? 4 : 16;
+    constexpr int kPer = kThreads / kLanes;   // groups per workgroup and pass
+    const int64_t groups = int64_t(T) * (H / (MX ? 32 : kGroup));
+    for (int64_t base = int64_t(blockIdx.x - 1) * kPer; base < groups; base += int64_t(gridDim.x - 1) * kPer) {
+        if constexpr (MX)
+            quant_group_mx(x, T, H, xq, static_cast<uint8_t*>(xs), base + threadIdx.x / kLanes,
+                           threadIdx.x % kLanes);
+        else
+            quant_group(x, T, H, xq, static_cast<float*>(xs), base + threadIdx.x / kLanes, threadIdx.x % kLanes);
     }
 }
 
@@ -397,6 +439,22 @@ hipError_t launch_align(const int32_t* ids, int T, int topk, int E, int block_m,
 int64_t align_scratch_bytes(int64_t R, int E) {
     const int64_t groups = (R + kWideSlots - 1) / kWideSlots;
     return 2 * groups * E * int64_t(sizeof(int32_t));
+}
+
+hipError_t launch_align_quant(const int32_t* ids, int T, int topk, int E, int block_m, int64_t cap,
+                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, const uint16_t* x, int H,
+                              uint8_t* xq, void* xs, bool mx, hipStream_t s) {
+    const int R = T * topk;
+    const int64_t groups = int64_t(T) * (H / (mx ? 32 : kGroup));
+    const int64_t per = kThreads / (mx ? 4 : 16);
+    const int64_t qwg = std::min<int64_t>(std::max<int64_t>((groups + per - 1) / per, 1), 2048);
+    const bool tiny = R <= kTinyMaxSlots;
+    void (*k)(const int32_t*, int, int, int, int, int32_t*, int32_t*, int32_t*, const uint16_t*, int, int,
+              uint8_t*, void*) = mx ? (tiny ? align_quant_kernel<true, true> : align_quant_kernel<true, false>)
+                                    : (tiny ? align_quant_kernel<false, true> : align_quant_kernel<false, false>);
+    hipLaunchKernelGGL(k, dim3(unsigned(1 + qwg)), dim3(kThreads), 0, s, ids, R, E, block_m, int(cap), sorted_ids,
+                       expert_ids, ntpp, x, T, H, xq, xs);
+    return hipGetLastError();
 }
 
 hipError_t launch_align_wide(const int32_t* ids, int T, int topk, int E, int block_m, int64_t cap,

@@ -283,6 +283,11 @@ hipError_t launch_decode_layer(const GemmArgs& g, int wdtype_fp8, int mx, const 
                                int32_t* expert_ids, int32_t* ntpp, int cap, uint8_t* xq, void* xs, uint16_t* out,
                                uint32_t* sync, hipStream_t s);
 
+// the one-workgroup alignment (up to kAlignWideMinSlots slots) and the fp8 /
+// MXFP8 quantisation of x in one launch (align.hip)
+hipError_t launch_align_quant(const int32_t* ids, int T, int topk, int E, int block_m, int64_t cap,
+                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, const uint16_t* x, int H,
+                              uint8_t* xq, void* xs, bool mx, hipStream_t s);
 hipError_t launch_combine(const float* y, bool bf16_y, const int32_t* ids, int T, int topk, int E, int H,
                           uint16_t* out, hipStream_t s);
 

@@ -342,14 +342,20 @@ int run_forward(const moe_forward_args* a, void* workspace, int64_t workspace_by
     int32_t* sorted = reinterpret_cast<int32_t*>(ws + p.off_sorted);
     int32_t* eids = reinterpret_cast<int32_t*>(ws + p.off_eids);
     int32_t* ntpp = reinterpret_cast<int32_t*>(ws + p.off_ntpp);
+    const bool wide = int64_t(a->T) * a->topk >= kAlignWideMinSlots;
+    // fp8 and MXFP8 with the one-workgroup alignment: the quantisation of x
+    // runs in the same launch on the other CUs (its stage time is then 0)
+    const bool joint = fp8 && !wide;
     const hipError_t ae =
-        int64_t(a->T) * a->topk >= kAlignWideMinSlots
-            ? launch_align_wide(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap, sorted, eids, ntpp, nullptr,
-                                ws + p.off_y, stream)
-            : launch_align(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap, sorted, eids, ntpp, nullptr, stream);
+        wide    ? launch_align_wide(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap, sorted, eids, ntpp, nullptr,
+                                    ws + p.off_y, stream)
+        : joint ? launch_align_quant(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap, sorted, eids, ntpp, g.x,
+                                     a->H, ws + p.off_xq, ws + p.off_xs, mx, stream)
+                : launch_align(a->topk_ids, a->T, a->topk, a->E, p.block_m, p.cap, sorted, eids, ntpp, nullptr,
+                               stream);
     if ((st = hip_status(ae)) != MOE_OK) return st;
     if ((st = mark(1)) != MOE_OK) return st;
-    if (fp8) {
+    if (fp8 && !joint) {
         const hipError_t qe = mx ? launch_quant_act_mx(g.x, a->T, a->H, ws + p.off_xq, ws + p.off_xs, stream)
                                  : launch_quant_act(g.x, a->T, a->H, ws + p.off_xq,
                                                     reinterpret_cast<float*>(ws + p.off_xs), stream);
