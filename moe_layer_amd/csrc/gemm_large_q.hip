@@ -504,10 +504,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_q_kernel(GemmArgs g, i
 // A workgroup with one column tile would spend most of its life on its
 // prologue and its y stores with no weight bytes in flight (two stages of
 // K = 128).  Here a workgroup keeps the block's token tile in LDS (one slot per
-// K stage, loaded once by group 1) and walks `ntw` adjacent column tiles; all
-// eight waves stream each tile's weights through the two weight slots (32 rows
-// per wave and stage), and a tile's y rows are stored while the next tile's
-// first weights load.  Same phases, barriers and waits as run_tile_q.
+// K stage, loaded once by group 1) and walks `ntw` adjacent column tiles.
+// Group 0 streams each tile's weights through the two weight slots; group 1
+// multiplies and stores token sub-tiles 0 and 1 and loads nothing after the
+// prologue, so its y stores never sit in front of a wait for weights (stores
+// count in the same vmcnt as loads).  With every wave loading and storing the
+// down GEMM took 100 / 355 us at 1024 / 8192 tokens of the fp8 layer, with
+// this split 97 / 343 us; a timing-only copy without the y stores 56 / 159 us,
+// and y rows staged through LDS into whole 128-byte lines ran slower (105 /
+// 411 us).  Group 0 multiplies sub-tiles 2 and 3 when a block has more than
+// 64 rows.
+// Same phases and barriers as run_tile_q.
 constexpr int kShortK = 256;
 constexpr int kShortMaxTiles = kMaxK / kTM;   // column tiles of the widest H
 
@@ -530,12 +537,12 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
     const uint8_t* wbase = static_cast<const uint8_t*>(g.w2) + (size_t(e) * g.H + size_t(tile0) * kTM) * kbytes;
     const uint8_t* bbase = static_cast<const uint8_t*>(g.inter) + size_t(blk) * kBM * kbytes;
     const uint32_t a_lane = uint32_t(lrow) * kbytes;
-    auto issue_a = [&](int s, lds_t* A) {   // every wave: 32 weight rows of stage s
+    auto issue_a = [&](int s, lds_t* A) {   // group 0: 64 weight rows per wave of stage s
         const int c = NST == 2 ? s >> 1 : s, k = s - c * NST;
         const uint8_t* base = wbase + size_t(c) * kTM * kbytes + k * kRowBytes;
 #pragma unroll
-        for (int q = 0; q < kLoadsA / 2; ++q) {
-            const int r0 = 32 * wv + kLoadRows * q;
+        for (int q = 0; q < kLoadsA; ++q) {
+            const int r0 = 64 * wm + kLoadRows * q;
             load_lds(base + size_t(r0) * kbytes, a_lane + ((q & 1) ? lchunk_odd : lchunk_even), A + r0 * kRowBytes);
         }
     };
@@ -554,7 +561,10 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
 #pragma unroll
     for (int t = 0; t < 8; ++t) coff[t] = swz_chunk(fr, t) + 8 * fk;
     const uint32_t a_row = uint32_t(64 * wm + fr) * kRowBytes;
-    const uint32_t b_row = uint32_t(32 * grp + fr) * kRowBytes;
+    // sub-tile u of a wave: token rows 32 st0 + 32 u .. (group 1 takes
+    // sub-tiles 0 and 1, group 0 sub-tiles 2 and 3)
+    const int st0 = grp == 1 ? 0 : 2;
+    const uint32_t b_row = uint32_t(32 * st0 + fr) * kRowBytes;
 
     // scales: block-scaled weights from the workgroup's LDS table [tile][128-row block][K stage];
     // MXFP8 weights per lane (E8M0 bytes of the fragment rows, 4 per stage)
@@ -587,7 +597,7 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
     float two[NU > 0 ? NU : 1];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        fo[u] = g.sorted_ids[blk * kBM + (2 * u + grp) * 32 + fr];
+        fo[u] = g.sorted_ids[blk * kBM + (st0 + u) * 32 + fr];
         two[u] = fo[u] < R ? gemm2_row_weight(g, fo[u]) : 0.0f;
     }
 
@@ -600,7 +610,7 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
 #pragma unroll
                 for (int a = 0; a < 2; ++a) af[a][j] = *reinterpret_cast<lds_v2*>(A + a_row + c + a * 32 * kRowBytes);
 #pragma unroll
-                for (int u = 0; u < NU; ++u) bfr[u][j] = *reinterpret_cast<lds_v2*>(B + b_row + c + u * 64 * kRowBytes);
+                for (int u = 0; u < NU; ++u) bfr[u][j] = *reinterpret_cast<lds_v2*>(B + b_row + c + u * 32 * kRowBytes);
             }
         }
     };
@@ -681,7 +691,7 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
             const int c = NST == 2 ? s >> 1 : s, k = s - c * NST;
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                const int row = 32 * (2 * u + grp) + fr;
+                const int row = 32 * (st0 + u) + fr;
                 if constexpr (MX) mb[u] = *reinterpret_cast<const uint32_t*>(ring.tscale + row * (K / 32) + 4 * k);
                 else sb[u] = reinterpret_cast<const float*>(ring.tscale)[row * NST + k];
             }
@@ -725,8 +735,10 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
         read_half(A, B, 0);
         stage_scales(s);
         if (more) {
-            issue_a(s + 1, An);
-            issue_ms(s + 1, Mn);
+            if (grp == 0) {
+                issue_a(s + 1, An);
+                issue_ms(s + 1, Mn);
+            }
             scales_for(s + 1);
         }
         wait_lgkm0();
@@ -735,17 +747,17 @@ __device__ __forceinline__ void run_tiles_q2(const GemmArgs& g, const RingQ& rin
         barrier();
         read_half(A, B, 1);
         wait_lgkm0();
-        if (grp == 1) wait_vm0();   // its weight loads (and scales) of the next stage
         barrier();
         compute(1);
         fold();
-        if (grp == 0) wait_vm0();
+        if (grp == 0) wait_vm0();   // the weights (and scales) of the next stage
         barrier();
     };
 
-    issue_a(0, ring.a[0]);
-    issue_ms(0, ring.ms[0]);
-    if (grp == 1) {
+    if (grp == 0) {
+        issue_a(0, ring.a[0]);
+        issue_ms(0, ring.ms[0]);
+    } else {
         issue_b(0, ring.b[0]);
         if constexpr (NST == 2) issue_b(1, ring.b[1]);
     }
@@ -818,7 +830,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm2_large_q_short_kernel(GemmAr
     __syncthreads();
     const int live = (s_valid + 31) >> 5;
     const int grp = (threadIdx.x >> 6) >> 2;
-    const int nu = (live - grp + 1) >> 1;
+    const int nu = grp == 1 ? min(live, 2) : max(0, min(live - 2, 2));
     switch (nu) {
         case 0: run_tiles_q2<MX, NST, 0>(g, ring, blk, tile0, ntw, e); break;
         case 1: run_tiles_q2<MX, NST, 1>(g, ring, blk, tile0, ntw, e); break;
