@@ -13,12 +13,14 @@
 //                        experts, stable scatter, tail; no scratch memory
 //   align_kernel         one workgroup of 16 waves (no scratch memory):
 //                        per-wave counts, scan, stable scatter, tail
-//   align_count_kernel   many workgroups of 4 waves x 256 slots: per-
-//   align_scan_kernel    workgroup counts to scratch; one workgroup scans
-//   align_scatter_kernel them into per-workgroup start positions, padding,
-//                        tail and block experts; many workgroups scatter.
-//                        Used when the slot count is large enough that one
-//                        CU's ALUs would be the bottleneck.
+//   align_count_kernel   many workgroups of 4 waves x 256 slots (1024 per
+//   align_scan_kernel    workgroup): per-workgroup counts to scratch; one
+//   align_scatter_kernel workgroup scans them into per-workgroup start
+//                        positions, padding, tail and block experts; many
+//                        workgroups scatter.  Used above 8192 slots, where
+//                        one CU's ALUs would be the bottleneck.
+// align_quant_kernel runs align_kernel (or the one-wave form) in workgroup 0
+// and the fp8 / MXFP8 quantisation of the layer input in the others.
 #include "dev_align.h"
 #include "dev_quant.h"
 

@@ -32,8 +32,10 @@
 // holds row l % 32 at K offset (l / 32) * 8).
 //
 // The block's token-row activation scales (per 128 K, or E8M0 per 32 K) sit in
-// an LDS table for the whole K; the weight scales are read per stage (block
-// scales: wave-uniform scalars; E8M0: one dword per lane and fragment).
+// an LDS table for the whole K, and so do the tile's block weight scales.
+// Packed MXFP8 weight scales arrive with each stage through LDS (one
+// direct-to-LDS load of the tile's 16 row groups); row-major ones are read per
+// lane, one dword per fragment row and stage.
 //
 //   GEMM1 (a4+a5): tile = 128 intermediate columns (one quantisation group):
 //                  gate rows c0..c0+127 and up rows I+c0..; epilogue a =
@@ -42,6 +44,9 @@
 //                  through LDS) or of each 32-column group (one wave's
 //                  columns), and e4m3 codes (P2 sections 1.1, 1.2).
 //   GEMM2 (a6):    tile = 256 output columns h; epilogue y[f] = bf16(tw[f] * acc).
+//                  For I <= 256 (one or two stages) a workgroup walks several
+//                  column tiles with the token tile resident in LDS
+//                  (gemm2_large_q_short_kernel, below).
 #include "common.h"
 
 namespace moe {
