@@ -171,6 +171,43 @@ def test_quant_act_mx_bit_exact():
     np.testing.assert_array_equal(codes.cpu().numpy(), c_o)
 
 
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("T", [16, 300, 1100])
+def test_forward_input_quant_in_workspace(wdtype, T):
+    """The layer input's e4m3 codes and scales that moe_forward leaves in its
+    workspace equal the oracle's bit for bit: quantised by the other
+    workgroups of the alignment's launch up to 8192 slots (16 tokens: the
+    one-wave alignment, 300: the one-workgroup form), by their own kernel
+    above (1100 tokens x 8 slots)."""
+    from moe_layer_amd.workloads import Config
+    k, H = 8, 512
+    cfg = Config("xq_" + wdtype, T, 8, H, 256, k, wdtype, "given")
+    layer = layer_for(cfg)
+    layer.ensure(range(8))
+    rng = np.random.default_rng(T)
+    x = (rng.standard_normal((T, H)) * 0.1).astype(np.float32)
+    x[0] = 0.0                                   # all-zero groups: the 1e-10 floor
+    x[1, :64] *= 1e-6                            # e4m3 subnormal codes
+    x[2, 128:256] *= 1e4
+    x[3, :128] = 1.75                            # the amax = 1.75 boundary
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ids = rng.integers(0, 8, size=(T, k)).astype(np.int32)
+    tw = np.full((T, k), 1.0 / k, np.float32)
+    out, ws, (xt, ids_t, tw_t) = run_forward(layer, bits, ids, tw)
+    p = ops.moe_plan(ops.forward_args(xt, layer.w13, layer.w2, ids_t, tw_t, layer.s13, layer.s2, out))
+    assert (T * k <= 8192) == (ops.moe_align_scratch_bytes(T, k, 8) == 0)
+    w = ws.cpu().numpy()
+    group = 32 if wdtype == "mxfp8" else 128
+    c_o, s_o, _ = O.quant_act(bits_to_bf16(bits).to(torch.float64).numpy(), group)
+    np.testing.assert_array_equal(w[p["off_xq"]: p["off_xq"] + T * H].reshape(T, H), c_o)
+    if wdtype == "mxfp8":
+        xs = w[p["off_xs"]: p["off_xs"] + T * (H // 32)].reshape(T, H // 32)
+        np.testing.assert_array_equal(xs, O.e8m0_encode(s_o))
+    else:
+        xs = w[p["off_xs"]: p["off_xs"] + 4 * T * (H // 128)].view(np.float32).reshape(T, H // 128)
+        np.testing.assert_array_equal(xs.astype(np.float64), s_o)
+
+
 # ----------------------------------------------------------------- forward ---
 
 def _forward_case(cfg, tokens=None, **kw):
