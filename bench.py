@@ -81,10 +81,15 @@ KERNEL_SOURCES = {"small": ("gemm_small.hip", "dev_gemm_small.h", "common.h"),
 
 
 def kernel_source_digest(path: str) -> str:
+    """sha256 prefix of the kernel's sources with their // comments and blank
+    lines removed (a comment edit does not change what the counters saw)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_layer_amd", "csrc")
     for name in KERNEL_SOURCES[path]:
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        for line in open(os.path.join(csrc, name), encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
