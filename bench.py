@@ -16,7 +16,9 @@ stream it runs on; ``layer`` the whole step against the layer's roofline;
 ``cpu_baseline`` is the fp64 oracle on a bounded token sample on this host.
 The default run (the decode layer) also times the prefill layer (T=4096,
 E=128, H=4096, I=1536, top-8, bf16) and adds it as ``prefill``: the metric's
-second half, its matrix-core fraction (``--no-prefill`` skips it).
+second half, its matrix-core fraction; and the block-fp8 layer (T=1024,
+E=256, H=4096, I=256, top-8, e4m3 weights with 128x128 scales) as ``fp8``.
+``--no-prefill`` skips both extra records, ``--no-fp8`` the fp8 one.
 """
 from __future__ import annotations
 
@@ -65,8 +67,11 @@ def parse():
                     help="run each step as one moe_decode_layer launch (routing inside the kernel)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the prefill record the default decode run adds")
+                    help="skip the prefill and fp8 records the default decode run adds")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the fp8-layer record the default decode run adds")
+    ap.add_argument("--fp8-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region run one plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -131,6 +136,22 @@ def main():
             "gemm1": {k: p["roofline"][k] for k in ("kernel", "kernel_ms", "mfma_frac", "hbm_frac", "traffic")},
             "gemm2_ms": p["layer"]["stage_ms"]["gemm2"], "stage_ms": p["layer"]["stage_ms"],
             "active_experts": p["layer"]["active_experts"],
+        }
+    if args.workload == "decode" and not args.tokens and not args.no_prefill and not args.no_fp8 \
+            and not args.decode_layer:
+        # the block-fp8 layer, timed in the same run
+        import gc
+        import torch
+        gc.collect()
+        torch.cuda.empty_cache()
+        q = measure(args, "fp8", None, args.fp8_steps, 3, False, False)
+        rec["fp8"] = {
+            "workload": q["config"]["workload"], "steps": q["steps"], "warmup": q["warmup"],
+            "path": q["config"]["path"], "ms_per_step": q["ms_per_step"], "tokens_per_s": q["value"],
+            "hbm_frac": q["layer"]["hbm_frac"], "mfma_frac": q["layer"]["mfma_frac"],
+            "roofline_frac": q["layer"]["roofline_frac"],
+            "gemm1": {k: q["roofline"][k] for k in ("kernel", "kernel_ms", "hbm_frac", "traffic")},
+            "stage_ms": q["layer"]["stage_ms"],
         }
     print(json.dumps(rec), flush=True)
 
