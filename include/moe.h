@@ -290,12 +290,14 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  *   SiLU-mul epilogue a = bf16(bf16(silu(bf16 h_gate)) * bf16 h_up)
  *   [fp8: + per-row 128-group pow2 scale and E4M3 codes], kept in sorted
  *   order (P2 sections 1.1 and 1.2) -> GEMM2 y = tw * (W2[e] . a) with the
- *   router weight applied in fp32 after the GEMM (P2 section 1.1) ->
+ *   router weight applied in fp32 after the GEMM (P2 section 1.1), one row
+ *   per slot, kept in fp32 (bf16 weights) or bf16 (fp8 and MXFP8 weights) ->
  *   out_t = bf16(sum_j y_{t,j}) summed in fp32 in slot order j = 0..topk-1
  *   (the expert aggregation of P1, "Backend-Wechsel").
  * MXFP8: the same with x and the intermediate quantised per row and
  * 32-group, scales as E8M0 bytes, and every 32-element block of a product
- * scaled by its two E8M0 scales inside the matrix-core instruction.
+ * scaled by its two E8M0 scales (inside the matrix-core instruction in the
+ * weight-streaming down GEMM, folded into exact bf16 conversions elsewhere).
  * fp8 and MXFP8 weights arrive pre-quantised with their scales; the library
  * never quantises weights.
  * Layer variants (P2 section 1.1 names both switches: the
@@ -325,7 +327,8 @@ MOE_API int64_t moe_forward_workspace(const moe_forward_args* a);
  * block_m names a size of the weight-streaming path (16, 32, 64); forcing it
  * elsewhere is MOE_ERR_UNSUPPORTED.
  * The workspace's activation scales (off_xs, off_inter_scale) are fp32 for
- * FP8_E4M3 and E8M0 bytes for MXFP8.  Unknown flag bits, and a clamp limit
+ * FP8_E4M3 and E8M0 bytes for MXFP8; its y rows (off_y, [T*topk, H] by flat
+ * slot) fp32 for bf16 weights and bf16 for FP8_E4M3 and MXFP8.  Unknown flag bits, and a clamp limit
  * that is negative or NaN, are MOE_ERR_INVALID_ARG.
  */
 MOE_API int moe_forward(const moe_forward_args* a, void* workspace, int64_t workspace_bytes,
