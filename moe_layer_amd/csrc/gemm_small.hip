@@ -38,6 +38,122 @@ __global__ __launch_bounds__(NW * 64) void gemm2_tiles_kernel(GemmArgs g, int ng
     gemm2_tiles<FP8, NT, WT, NW, U, NTILE>(g, blk, grp * NTILE);
 }
 
+// ----------------------------------------------------------------------------
+// Down GEMM (a6) for 16-row blocks, its weights streamed through LDS.
+//
+// gemm2_small_kernel loads every lane's 16-byte operand pieces straight into
+// registers, so each load instruction touches 32 bytes of 16 different W2
+// rows.  Here the weights move global -> LDS with direct-to-LDS loads (lane
+// i's 16 bytes land at the instruction's LDS base + 16 i), each instruction
+// covering 8 whole 128-byte row pieces, through a kNB-slot ring kNB - 1 stages
+// deep.  A workgroup of 4 waves owns 64 output rows (16 per wave) of one
+// expert block; a stage is 64 K (two MFMA steps); the block's 16 token rows of
+// the stage ride in the same slot (rows 64..79; the second 8-row group only
+// when it holds a routed row).  Waves 0..3 each load 16 weight rows, waves 0
+// and 1 one token group: each waits for its own loads, then one barrier per
+// stage publishes the slot and frees the slot read in the previous stage.
+// LDS rows are 128 bytes with chunk c of row r at position c ^ ((r >> 1) & 7),
+// so a fragment read (16 rows at one chunk) hits distinct banks.
+//
+// Operands, MFMA (16x16x32 bf16), K order and epilogue are gemm2_small_tile's
+// for one 16-token tile, so y is bitwise the same.
+// ----------------------------------------------------------------------------
+constexpr int kLdsRows = 64;                       // output rows per workgroup
+constexpr int kLdsRowBytes = 128;                  // K bytes of a row per stage
+constexpr int kLdsSlot = (kLdsRows + 16) * kLdsRowBytes;
+
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// wait until at most `ahead` stages of NLD loads each are still in flight
+template <int NLD, int MAXA>
+__device__ __forceinline__ void wait_stages(int ahead) {
+    if constexpr (MAXA <= 0) {
+        wait_vm_n<0>();
+    } else {
+        if (ahead >= MAXA) wait_vm_n<MAXA * NLD>();
+        else wait_stages<NLD, MAXA - 1>(ahead);
+    }
+}
+
+template <int kNB>
+__global__ __launch_bounds__(256) void gemm2_lds_kernel(GemmArgs g, int ntiles) {
+    typedef __attribute__((address_space(3))) uint8_t lds_t;
+    typedef const __attribute__((address_space(3))) i32x4 lds_v4;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kNB * kLdsSlot];
+    constexpr int D = kNB - 1;
+    int blk, tile;
+    if (!map_active_tile<true>(g, ntiles, blk, tile)) return;
+    const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
+    if (e < 0) return;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = g.H, I = g.I, R = g.T * g.topk;
+    const int nst = I / 64;
+    const int h0 = tile * kLdsRows;
+    const int lr = lane & 15, lk = lane >> 4;
+
+    // this lane's token row of the block; rows 8..15 loaded only if one is routed
+    const int f = g.sorted_ids[blk * 16 + lr];
+    const bool upper = (__ballot(f < R) & 0xff00ull) != 0;
+    const bool tok_loader = wv == 0 || (wv == 1 && upper);
+
+    // load sources: load q of wave w fills LDS rows 16 w + 8 q + lane / 8 at
+    // position lane % 8, the token group t rows 64 + 8 t + lane / 8; both with
+    // chunk (lane % 8) ^ ((row >> 1) & 7) = (lane % 8) ^ ((lane / 16 + 4 q) % 8)
+    const uint32_t ch0 = uint32_t((lane & 7) ^ ((lane >> 4) & 7)) << 4;
+    const uint32_t ch1 = uint32_t((lane & 7) ^ (((lane >> 4) + 4) & 7)) << 4;
+    const size_t rowb = size_t(I) * 2;
+    const uint8_t* wsrc = static_cast<const uint8_t*>(g.w2) + (size_t(e) * H + h0 + wv * 16 + (lane >> 3)) * rowb;
+    const uint8_t* tsrc = static_cast<const uint8_t*>(g.inter) + (size_t(blk) * 16 + wv * 8 + (lane >> 3)) * rowb +
+                          ((wv & 1) ? ch1 : ch0);
+    auto issue = [&](int st) {
+        lds_t* slot = (lds_t*)(ring) + (st % kNB) * kLdsSlot;
+        const size_t k0 = size_t(st) * kLdsRowBytes;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wsrc + k0 + ch0), slot + wv * 2048, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wsrc + 8 * rowb + k0 + ch1),
+                                         slot + wv * 2048 + 1024, 16, 0, 0);
+        if (tok_loader)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tsrc + k0),
+                                             slot + kLdsRows * kLdsRowBytes + wv * 1024, 16, 0, 0);
+    };
+    // fragment reads: row r at chunk 4 j + lane / 16 (MFMA step j of the stage)
+    const int arow = wv * 16 + lr, brow = kLdsRows + lr;
+    uint32_t aoff[2], boff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        aoff[j] = uint32_t(arow * kLdsRowBytes + (((4 * j + lk) ^ ((arow >> 1) & 7)) << 4));
+        boff[j] = uint32_t(brow * kLdsRowBytes + (((4 * j + lk) ^ ((brow >> 1) & 7)) << 4));
+    }
+
+    f32x4 acc = {0, 0, 0, 0};
+    for (int st = 0; st < D && st < nst; ++st) issue(st);
+    for (int s = 0; s < nst; ++s) {
+        const int ahead = min(s + D - 1, nst - 1) - s;   // stages issued beyond s
+        if (tok_loader) wait_stages<3, D - 1>(ahead);
+        else wait_stages<2, D - 1>(ahead);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + D < nst) issue(s + D);
+        const lds_t* slot = (const lds_t*)(ring) + (s % kNB) * kLdsSlot;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const i32x4 a = *reinterpret_cast<lds_v4*>(slot + aoff[j]);
+            const i32x4 b = *reinterpret_cast<lds_v4*>(slot + boff[j]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                          acc, 0, 0, 0);
+        }
+    }
+    if (f >= R) return;
+    const float tw = gemm2_row_weight(g, f);
+    f32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __fmul_rn(acc[j], tw);
+    store_y4<false>(g.y, int64_t(f) * H + h0 + wv * 16 + 4 * lk, v);
+}
+
 template <typename K>
 hipError_t launch_tiles(K kernel, const GemmArgs& g, int ntiles, int threads, hipStream_t s) {
     const int64_t n = int64_t(g.num_blocks) * ntiles;
@@ -104,14 +220,18 @@ hipError_t gemm2_dispatch(const GemmArgs& g, hipStream_t s) {
         // K = I is short: 64 output rows per wave keep more bytes in flight
         // (32 for 64-token blocks, registers; 32 when H % 256 != 0)
         if constexpr (NT <= 2) {
-            if (small_gemm2_cols(g.T, g.topk, g.E, g.H, true, NT) == 256) return gemm2_fp8<NT, 4>(g, s);
+            if (small_gemm2_cols(g.T, g.topk, g.E, g.H, g.I, true, NT) == 256) return gemm2_fp8<NT, 4>(g, s);
         }
         return gemm2_fp8<NT, 2>(g, s);
     } else {
-        // 128 output columns per workgroup, or 64 when H is not a multiple of
-        // 128 (narrower tiles for one or two decode tokens measured slower);
-        // 256 when a single token's experts leave the grid short of waves
-        const int cols = small_gemm2_cols(g.T, g.topk, g.E, g.H, false, NT);
+        // 16-row blocks stream their weights through LDS (gemm2_lds_kernel);
+        // otherwise 128 output columns per workgroup, or 64 when H is not a
+        // multiple of 128; 256 when a single token's experts leave the grid
+        // short of waves
+        if constexpr (NT == 1) {
+            if (gemm2_lds_supported(g.H, g.I)) return launch_tiles(gemm2_lds_kernel<4>, g, g.H / kLdsRows, 256, s);
+        }
+        const int cols = small_gemm2_cols(g.T, g.topk, g.E, g.H, g.I, false, NT);
         if (cols == 256) return gemm2_bf16<NT, 4>(g, s);
         if (cols == 128) return gemm2_bf16<NT, 2>(g, s);
         return gemm2_bf16<NT, 1>(g, s);
@@ -120,11 +240,14 @@ hipError_t gemm2_dispatch(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
+bool gemm2_lds_supported(int H, int I) { return H % kLdsRows == 0 && I % 64 == 0; }
+
 // GEMM2 output rows of H per workgroup on the weight-streaming path (the
 // dispatch above follows the same rule)
-int small_gemm2_cols(int T, int topk, int E, int H, bool fp8, int NT) {
+int small_gemm2_cols(int T, int topk, int E, int H, int I, bool fp8, int NT) {
     (void)E;
     if (fp8) return (NT <= 2 && H % 256 == 0) ? 256 : 128;
+    if (NT == 1 && gemm2_lds_supported(H, I)) return kLdsRows;   // gemm2_lds_kernel
     // at most 8 routed rows (one decode token): 64 output rows per wave ran
     // 12 % faster than 32 (one token, 8 of 256 experts, H 7168, I 2048), and
     // slower from 4 tokens on
