@@ -154,6 +154,126 @@ __global__ __launch_bounds__(256) void gemm2_lds_kernel(GemmArgs g, int ntiles) 
     store_y4<false>(g.y, int64_t(f) * H + h0 + wv * 16 + 4 * lk, v);
 }
 
+// ----------------------------------------------------------------------------
+// fp8 (128x128 block scales) down GEMM of 16-row blocks through LDS.
+//
+// The weights stream as in gemm2_lds_kernel (4 waves x 16 rows of a 64-row
+// column tile, two direct-to-LDS loads of 8 whole 128-byte row pieces per wave
+// and stage, a kNB-slot ring); a stage is one 128-K weight-scale block of one
+// tile.  K = I is short (up to 256 here: two stages), so a workgroup walks
+// kLdsQTiles adjacent column tiles of its block as one stream of stages,
+// storing each tile when its last block is in.  The block's 16
+// token rows (all of I, with their group scales) and the weight-block scales
+// of the workgroup's rows are staged in LDS once.  Per tile the arithmetic is
+// gemm2_tiles' (one fp8 MFMA per 128-K block, its sums scaled by weight-block
+// x token-group scale with one fma), so y is bitwise the same.  Measured on
+// the fp8 layer (E 256, H 4096, I 256) at 64 / 256 / 512 tokens, down GEMM
+// 56 / 70 / 83 us in registers, 53 / 65 / 71 us here (512 rows per workgroup,
+// a 3-slot ring: the smallest LDS footprint, most workgroups per CU, measured
+// best among 128-1024 rows and 3-6 slots).
+// ----------------------------------------------------------------------------
+constexpr int kLdsQTiles = 8;                     // column tiles per workgroup (512 output rows)
+constexpr int kLdsQMaxKb = 2;                     // I <= 256 (LDS for more workgroups per CU)
+constexpr int kLdsQSlot = kLdsRows * kLdsRowBytes;
+constexpr int kLdsQTok = kLdsQMaxKb * 16 * kLdsRowBytes;                  // the block's token rows
+constexpr int kLdsQWsc = kLdsQTiles * kLdsRows / kGroup * kLdsQMaxKb;     // weight-block scales (floats)
+constexpr int kLdsQTsc = 16 * kLdsQMaxKb;                                 // token-group scales (floats)
+
+template <int kNB>
+__global__ __launch_bounds__(256) void gemm2_lds_fp8_kernel(GemmArgs g, int ngroups) {
+    typedef __attribute__((address_space(3))) uint8_t lds_t;
+    typedef const __attribute__((address_space(3))) i32x4 lds_v4;
+    // one LDS object (ring, token rows, scale tables): with several, the
+    // compiler waits for every direct-to-LDS load before each LDS read
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kNB * kLdsQSlot + kLdsQTok + 4 * (kLdsQWsc + kLdsQTsc)];
+    uint8_t* tok = ring + kNB * kLdsQSlot;
+    float* wsc = reinterpret_cast<float*>(tok + kLdsQTok);
+    float* tsc = wsc + kLdsQWsc;
+    constexpr int D = kNB - 1;
+    int blk, grp;
+    if (!map_active_tile<true>(g, ngroups, blk, grp)) return;
+    const int e = __builtin_amdgcn_readfirstlane(g.expert_ids[blk]);
+    if (e < 0) return;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = g.H, I = g.I, R = g.T * g.topk;
+    const int nkb = I / kGroup;
+    const int V = kLdsQTiles * nkb;                 // stages: tile t = v / nkb, K block v % nkb
+    const int h00 = grp * kLdsQTiles * kLdsRows;    // first output row of the workgroup
+    const int lr = lane & 15, lk = lane >> 4;
+
+    const int f = g.sorted_ids[blk * 16 + lr];
+    const bool upper = (__ballot(f < R) & 0xff00ull) != 0;
+    const float tw = f < R ? gemm2_row_weight(g, f) : 0.0f;
+
+    // scale tables: weight blocks of the workgroup's 8 row blocks, the tokens' groups
+    const float* w2s = static_cast<const float*>(g.w2_scale) + (size_t(e) * (H / kGroup) + h00 / kGroup) * nkb;
+    for (int i = threadIdx.x; i < (kLdsQTiles * kLdsRows / kGroup) * nkb; i += 256) wsc[i] = w2s[i];
+    for (int i = threadIdx.x; i < 16 * nkb; i += 256) tsc[i] = g.inter_scale[size_t(blk) * 16 * nkb + i];
+
+    // load sources (as in gemm2_lds_kernel): chunk (lane % 8) ^ ((lane / 16 + 4 q) % 8)
+    const uint32_t ch0 = uint32_t((lane & 7) ^ ((lane >> 4) & 7)) << 4;
+    const uint32_t ch1 = uint32_t((lane & 7) ^ (((lane >> 4) + 4) & 7)) << 4;
+    // the token tile: K block k, 8-row group q at LDS rows 16 k + 8 q + lane / 8
+    const uint8_t* inter = static_cast<const uint8_t*>(g.inter) + (size_t(blk) * 16 + (lane >> 3)) * I;
+    for (int i = wv; i < 2 * nkb; i += 4) {
+        const int k = i >> 1, q = i & 1;
+        if (q == 1 && !upper) continue;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(inter + size_t(8 * q) * I + k * kGroup +
+                                                                       (q ? ch1 : ch0)),
+                                         (lds_t*)(tok) + (16 * k + 8 * q) * kLdsRowBytes, 16, 0, 0);
+    }
+    const uint8_t* wsrc = static_cast<const uint8_t*>(g.w2) + (size_t(e) * H + h00 + wv * 16 + (lane >> 3)) * I;
+    auto issue = [&](int v) {
+        const int t = v / nkb, k = v - t * nkb;
+        lds_t* slot = (lds_t*)(ring) + (v % kNB) * kLdsQSlot + wv * 2048;
+        const uint8_t* src = wsrc + size_t(t) * kLdsRows * I + k * kGroup;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + ch0), slot, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + size_t(8) * I + ch1), slot + 1024, 16, 0,
+                                         0);
+    };
+    for (int v = 0; v < D && v < V; ++v) issue(v);
+    wait_vm_n<0>();
+    __syncthreads();
+
+    // fragment reads: the lane's 32 bytes (chunks 2 lk, 2 lk + 1) of row r
+    const int arow = wv * 16 + lr;
+    const uint32_t a0 = uint32_t(arow * kLdsRowBytes + (((2 * lk) ^ ((arow >> 1) & 7)) << 4));
+    const uint32_t a1 = uint32_t(arow * kLdsRowBytes + (((2 * lk + 1) ^ ((arow >> 1) & 7)) << 4));
+    f32x4 acc = {0, 0, 0, 0};
+    for (int v = 0; v < V; ++v) {
+        const int ahead = min(v + D - 1, V - 1) - v;
+        wait_stages<2, D - 1>(ahead);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (v + D < V) issue(v + D);
+        const int t = v / nkb, k = v - t * nkb;
+        const lds_t* slot = (const lds_t*)(ring) + (v % kNB) * kLdsQSlot;
+        const int brow = 16 * k + lr;
+        const lds_t* tb = (const lds_t*)(tok) + brow * kLdsRowBytes;
+        const i32x4 x0 = *reinterpret_cast<lds_v4*>(slot + a0);
+        const i32x4 x1 = *reinterpret_cast<lds_v4*>(slot + a1);
+        const i32x4 y0 = *reinterpret_cast<lds_v4*>(tb + (((2 * lk) ^ ((brow >> 1) & 7)) << 4));
+        const i32x4 y1 = *reinterpret_cast<lds_v4*>(tb + (((2 * lk + 1) ^ ((brow >> 1) & 7)) << 4));
+        const i32x8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const i32x8 bv = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4{0, 0, 0, 0}, 0, 0, 0, 0, 0, 0);
+        const float c = __fmul_rn(wsc[((t * kLdsRows + wv * 16) / kGroup) * nkb + k], tsc[lr * nkb + k]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(p[j], c, acc[j]);
+        if (k == nkb - 1) {
+            if (f < R) {
+                f32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = __fmul_rn(acc[j], tw);
+                store_y4<true>(g.y, int64_t(f) * H + h00 + t * kLdsRows + wv * 16 + 4 * lk, o);
+            }
+            acc = f32x4{0, 0, 0, 0};
+        }
+    }
+}
+
 template <typename K>
 hipError_t launch_tiles(K kernel, const GemmArgs& g, int ntiles, int threads, hipStream_t s) {
     const int64_t n = int64_t(g.num_blocks) * ntiles;
@@ -219,6 +339,10 @@ hipError_t gemm2_dispatch(const GemmArgs& g, hipStream_t s) {
     if constexpr (FP8) {
         // K = I is short: 64 output rows per wave keep more bytes in flight
         // (32 for 64-token blocks, registers; 32 when H % 256 != 0)
+        if constexpr (NT == 1) {
+            if (gemm2_lds_fp8_supported(g.H, g.I))
+                return launch_tiles(gemm2_lds_fp8_kernel<3>, g, g.H / (kLdsQTiles * kLdsRows), 256, s);
+        }
         if constexpr (NT <= 2) {
             if (small_gemm2_cols(g.T, g.topk, g.E, g.H, g.I, true, NT) == 256) return gemm2_fp8<NT, 4>(g, s);
         }
@@ -241,11 +365,15 @@ hipError_t gemm2_dispatch(const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 bool gemm2_lds_supported(int H, int I) { return H % kLdsRows == 0 && I % 64 == 0; }
+bool gemm2_lds_fp8_supported(int H, int I) {
+    return H % (kLdsQTiles * kLdsRows) == 0 && I % kGroup == 0 && I / kGroup <= kLdsQMaxKb;
+}
 
 // GEMM2 output rows of H per workgroup on the weight-streaming path (the
 // dispatch above follows the same rule)
-int small_gemm2_cols(int T, int topk, int E, int H, int I, bool fp8, int NT) {
+int small_gemm2_cols(int T, int topk, int E, int H, int I, bool fp8, int NT, bool mx) {
     (void)E;
+    if (fp8 && !mx && NT == 1 && gemm2_lds_fp8_supported(H, I)) return kLdsRows;   // gemm2_lds_fp8_kernel
     if (fp8) return (NT <= 2 && H % 256 == 0) ? 256 : 128;
     if (NT == 1 && gemm2_lds_supported(H, I)) return kLdsRows;   // gemm2_lds_kernel
     // at most 8 routed rows (one decode token): 64 output rows per wave ran

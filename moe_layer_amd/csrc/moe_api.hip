@@ -118,7 +118,7 @@ int make_plan(const moe_forward_args* a, Plan* p) {
         p->gemm2_cols = 256;
     } else {
         p->gemm1_cols = fp8 ? 256 : 128;   // gate + up rows per workgroup
-        p->gemm2_cols = small_gemm2_cols(a->T, a->topk, a->E, a->H, a->I, fp8, bm / 16);   // same tiles for MXFP8
+        p->gemm2_cols = small_gemm2_cols(a->T, a->topk, a->E, a->H, a->I, fp8, bm / 16, mx);
     }
 
     const int64_t rows = int64_t(p->num_blocks) * bm;   // every row a block can touch

@@ -452,6 +452,20 @@ def test_rotated_k_walk_parity_and_block_m_invariance(wdtype):
             assert torch.equal(out, ref), f"block_m={bm}"
 
 
+@pytest.mark.parametrize("T", [256, 512])
+def test_fp8_16_row_blocks_lds_down_gemm(T):
+    """256 and 512 tokens of the fp8 layer on 16-row blocks (the down GEMM
+    streams W2 through LDS, 512 output rows per workgroup): oracle parity on
+    sampled tokens, and the same bits as the register-streaming down GEMM of
+    32-row blocks."""
+    cfg = CONFIGS["fp8"].with_tokens(T)
+    _forward_case(cfg, tokens=np.arange(0, T, 37))
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    a, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=16)
+    b, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=32)
+    assert torch.equal(a, b)
+
+
 def test_pack_mx_scales_layout():
     """moe_pack_mx_scales against its definition written as a numpy reshape:
     packed[((e*rows/16 + t)*K/128 + s)*64 + g*16 + r] = scales[e, 16t + r, 4s + g]."""
