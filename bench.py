@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill and fp8 records the default decode run adds")
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the fp8-layer record the default decode run adds")
     ap.add_argument("--fp8-steps", type=int, default=20)
@@ -122,12 +122,12 @@ def main():
                   args.copy_calibration)
     if args.workload == "decode" and not args.tokens and not args.no_prefill and not args.decode_layer:
         # the metric's prefill half: the prefill layer's matrix-core fraction,
-        # timed in the same run (fewer steps: 2 ms each)
+        # timed in the same run (20 steps after 5 of warm-up, ~2 ms each)
         import gc
         import torch
         gc.collect()
         torch.cuda.empty_cache()
-        p = measure(args, "prefill", None, args.prefill_steps, 2, False, False)
+        p = measure(args, "prefill", None, args.prefill_steps, 5, False, False)
         rec["prefill"] = {
             "workload": p["config"]["workload"], "steps": p["steps"], "warmup": p["warmup"],
             "ms_per_step": p["ms_per_step"], "tokens_per_s": p["value"],
@@ -144,7 +144,7 @@ def main():
         import torch
         gc.collect()
         torch.cuda.empty_cache()
-        q = measure(args, "fp8", None, args.fp8_steps, 3, False, False)
+        q = measure(args, "fp8", None, args.fp8_steps, 5, False, False)
         rec["fp8"] = {
             "workload": q["config"]["workload"], "steps": q["steps"], "warmup": q["warmup"],
             "path": q["config"]["path"], "ms_per_step": q["ms_per_step"], "tokens_per_s": q["value"],
