@@ -264,7 +264,8 @@ typedef struct moe_plan_info {
     int64_t capacity;      /* sorted rows incl. worst-case padding */
     int32_t num_blocks;    /* ceil(capacity / block_m): GEMM grid rows */
     int32_t gemm1_cols;    /* GEMM1 weight rows (of 2I, gate + up) per workgroup */
-    int32_t gemm2_cols;    /* GEMM2 weight rows (of H) per workgroup */
+    int32_t gemm2_cols;    /* GEMM2 weight rows (of H) per column tile; a workgroup
+                              may walk several adjacent tiles of its block */
     int32_t decode_layer;  /* 1 if moe_decode_layer takes these arguments */
     int64_t workspace_bytes;
     /* byte offsets of the forward's intermediates inside the workspace */
