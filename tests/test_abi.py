@@ -121,6 +121,25 @@ def test_plan_block_override_and_path():
     assert p["path"] == ops.MOE_PATH_SMALL_M and p["block_m"] == 64
 
 
+def test_plan_column_tiles():
+    """GEMM2 column-tile widths the planner reports for the weight-streaming
+    path: 16-row blocks stream W2 through LDS in 64-row tiles (every bf16
+    shape, whose H and I are multiples of 64; block fp8 for I <= 256 and H a
+    multiple of 512); other blocks, fp8 shapes and MXFP8 keep the
+    register-streaming tiles."""
+    assert ops.moe_plan(_args())["gemm2_cols"] == 64                        # decode, bf16, 16-row blocks
+    assert ops.moe_plan(_args(block_m=32))["gemm2_cols"] == 128
+    assert ops.moe_plan(_args(T=1, E=256, H=7168, I=2048))["gemm2_cols"] == 64
+    fp8 = dict(T=64, E=256, H=4096, I=256, k=8)
+    assert ops.moe_plan(_args(**fp8, wdtype=1))["block_m"] == 16
+    assert ops.moe_plan(_args(**fp8, wdtype=1))["gemm2_cols"] == 64
+    assert ops.moe_plan(_args(**dict(fp8, I=512), wdtype=1))["gemm2_cols"] == 256
+    assert ops.moe_plan(_args(**dict(fp8, H=4352), wdtype=1))["gemm2_cols"] == 256   # H % 512 != 0
+    assert ops.moe_plan(_args(**fp8, wdtype=2))["gemm2_cols"] == 256        # MXFP8
+    assert ops.moe_plan(_args())["gemm1_cols"] == 128
+    assert ops.moe_plan(_args(**fp8, wdtype=1))["gemm1_cols"] == 256
+
+
 def test_plan_large_path_limits():
     L = ops.lib()
     info = ops.PlanInfo()
