@@ -434,6 +434,23 @@ def test_block_m_invariance_bitwise(name, wdtype):
             assert torch.equal(out, ref), f"block_m={bm}"
 
 
+def test_block_m_invariance_skew_full_blocks():
+    """64 tokens of the skewed layer: its hot experts fill whole 16-row blocks,
+    so the down GEMM of 16-row blocks (weights through LDS) also loads the
+    blocks' second 8-row token group; the output is bit-identical to that of
+    the 32- and 64-row blocks (register-streaming down GEMM)."""
+    cfg = CONFIGS["skew"].with_tokens(64)
+    wl, layer, ids, tw = _layer_inputs(cfg)
+    assert np.bincount(ids.ravel(), minlength=cfg.E).max() > 8
+    ref = None
+    for bm in (16, 32, 64):
+        out, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=bm)
+        if ref is None:
+            ref = out.clone()
+        else:
+            assert torch.equal(out, ref), f"block_m={bm}"
+
+
 @pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
 def test_rotated_k_walk_parity_and_block_m_invariance(wdtype):
     """64 tokens of the fp8 / MXFP8 layer (2 routed rows per expert: GEMM1's
