@@ -385,6 +385,30 @@ def test_forward_ragged_shapes(wdtype):
         assert excess <= TAU[wdtype]
 
 
+@pytest.mark.parametrize("wdtype,H,I", [("bf16", 128, 64), ("bf16", 192, 128), ("fp8", 512, 128), ("fp8", 1024, 256)])
+def test_forward_short_k_16_row_blocks(wdtype, H, I):
+    """Down GEMMs of 16-row blocks whose K walk is shorter than their LDS ring
+    (bf16: one or two stages of 64; block fp8: one or two scale blocks):
+    oracle parity, and the same bits as the 32-row register-streaming form."""
+    from moe_layer_amd.workloads import Config
+    cfg = Config("short_k", 40, 8, H, I, 2, wdtype, "given")
+    wl = Workload(cfg)
+    rng = np.random.default_rng(11)
+    ids = np.stack([rng.permutation(8)[:2] for _ in range(40)]).astype(np.int32)
+    ids[:20, 0] = 3                      # one expert with a full 16-row block and more
+    ids[:20, 1] = np.where(ids[:20, 1] == 3, 4, ids[:20, 1])
+    tw = rng.random((40, 2)).astype(np.float32)
+    layer = layer_for(cfg)
+    layer.ensure(range(8))
+    a, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=16)
+    b, _, _ = run_forward(layer, wl.x_bf16_bits(), ids, tw, block_m=32)
+    assert torch.equal(a, b)
+    o = oracle_tokens(layer, wl.x_exact(), ids, tw.astype(np.float64), np.arange(40))
+    excess, raw, _ = compare_output(a.to(torch.float64).cpu().numpy(), o)
+    log(f"short K {wdtype} H={H} I={I}: excess/RMS={excess:.3e} raw={raw:.3e}")
+    assert excess <= TAU[wdtype]
+
+
 @pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
 @pytest.mark.parametrize("H,I", [(8448, 384), (8320, 256)])
 def test_forward_fp8_long_k(H, I, wdtype):
