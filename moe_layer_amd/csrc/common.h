@@ -262,7 +262,7 @@ __device__ __forceinline__ bool map_active_tile(const GemmArgs& g, int ntiles, i
 }
 
 hipError_t launch_gemm1_small(const GemmArgs& g, bool fp8, hipStream_t s);
-// NT = block_m / 16; mx: MXFP8 weights (their own kernels), else fp8 = block-scaled
+// NT = block_m / 16; mx: MXFP8 weights (their own kernels, the same tiles), else fp8 = block-scaled
 int small_gemm2_cols(int T, int topk, int E, int H, int I, bool fp8, int NT, bool mx = false);
 bool gemm2_lds_supported(int H, int I);       // bf16 down GEMM of 16-row blocks through LDS
 bool gemm2_lds_fp8_supported(int H, int I);   // its block-fp8 form

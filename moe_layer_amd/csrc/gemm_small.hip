@@ -373,7 +373,9 @@ bool gemm2_lds_fp8_supported(int H, int I) {
 // dispatch above follows the same rule)
 int small_gemm2_cols(int T, int topk, int E, int H, int I, bool fp8, int NT, bool mx) {
     (void)E;
-    if (fp8 && !mx && NT == 1 && gemm2_lds_fp8_supported(H, I)) return kLdsRows;   // gemm2_lds_fp8_kernel
+    // gemm2_lds_fp8_kernel, and gemm2_mx_lds_kernel (gemm_mx.hip) on the same shapes
+    (void)mx;
+    if (fp8 && NT == 1 && gemm2_lds_fp8_supported(H, I)) return kLdsRows;
     if (fp8) return (NT <= 2 && H % 256 == 0) ? 256 : 128;
     if (NT == 1 && gemm2_lds_supported(H, I)) return kLdsRows;   // gemm2_lds_kernel
     // at most 8 routed rows (one decode token): 64 output rows per wave ran

@@ -124,8 +124,8 @@ def test_plan_block_override_and_path():
 def test_plan_column_tiles():
     """GEMM2 column-tile widths the planner reports for the weight-streaming
     path: 16-row blocks stream W2 through LDS in 64-row tiles (every bf16
-    shape, whose H and I are multiples of 64; block fp8 for I <= 256 and H a
-    multiple of 512); other blocks, fp8 shapes and MXFP8 keep the
+    shape, whose H and I are multiples of 64; block fp8 and MXFP8 for I <= 256
+    and H a multiple of 512); other blocks and fp8 shapes keep the
     register-streaming tiles."""
     assert ops.moe_plan(_args())["gemm2_cols"] == 64                        # decode, bf16, 16-row blocks
     assert ops.moe_plan(_args(block_m=32))["gemm2_cols"] == 128
@@ -135,7 +135,8 @@ def test_plan_column_tiles():
     assert ops.moe_plan(_args(**fp8, wdtype=1))["gemm2_cols"] == 64
     assert ops.moe_plan(_args(**dict(fp8, I=512), wdtype=1))["gemm2_cols"] == 256
     assert ops.moe_plan(_args(**dict(fp8, H=4352), wdtype=1))["gemm2_cols"] == 256   # H % 512 != 0
-    assert ops.moe_plan(_args(**fp8, wdtype=2))["gemm2_cols"] == 256        # MXFP8
+    assert ops.moe_plan(_args(**fp8, wdtype=2))["gemm2_cols"] == 64         # MXFP8
+    assert ops.moe_plan(_args(**dict(fp8, I=512), wdtype=2))["gemm2_cols"] == 256
     assert ops.moe_plan(_args())["gemm1_cols"] == 128
     assert ops.moe_plan(_args(**fp8, wdtype=1))["gemm1_cols"] == 256
 
